@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the perception-encoder attention on one MI355X.
+
+One step = the whole 50-layer attention schedule of the ViT-G/14 tower at 4096
+patch tokens (64x64 grid): 13 full-attention layers (one 4096-token segment) and 37
+window layers (four 32x32 = 1024-token windows), H=16, head_dim=96, bf16 inputs with
+f32 accumulation, fresh seeded N(0,1) Q/K/V per layer, all resident in HBM before
+timing.  Layer kinds follow vllm.cpp issue #1545, second comment ("Two of the three
+labelled uncertainties are now resolved").
+
+Prints ONE JSON line: algorithmic TFLOP/s over the whole step (4*S^2*d*H per
+segment), ms per step (= ms per tower), the roofline of the attention kernel (HIP
+events around each launch on the launch stream), and the f64 CPU oracle timed on a
+bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "attention TFLOP/s (%bf16 MFMA peak) + ms per 50-layer tower attn @4096 tok"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published 2.5 PFLOP/s): 256 CU x 4096 FLOP/clk x 2.4 GHz
+KERNEL_NAME = "attn_fwd_bf16<96>"
+TRAFFIC_FILE = ROOT / "profiles" / "attn_fwd_bf16_96_tower4096_traffic.json"
+KERNEL_SOURCES = ["vit_perception_encoder_amd/csrc/attn_bf16.hpp", "vit_perception_encoder_amd/csrc/plan.hpp",
+                  "vit_perception_encoder_amd/csrc/mgattn.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if
+    it is missing or was taken on a different kernel source."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    t = json.loads(TRAFFIC_FILE.read_text())
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(layer_case):
+    """The f64 oracle, as it stands, on one whole 4096-token full-attention layer."""
+    from oracle import oracle as orc
+
+    c = layer_case
+    q, k, v = (x.reshape(c.T, c.H, c.d) for x in (c.q, c.k, c.v))
+    threads = host_threads()
+    t0 = time.perf_counter()
+    out = orc.attention(q, k, v, c.cu_seqlens, c.H, c.d, c.scale, n_threads=threads)
+    dt = time.perf_counter() - t0
+    return out, {"value": c.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                 "seconds": dt,
+                 "sample": f"one full-attention layer ({c.name}: 1 segment x 4096 tokens, H=16, d=96, "
+                           f"bf16 inputs widened to f64), whole output, {c.flops() / 1e9:.1f} GFLOP"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from vit_perception_encoder_amd import mgattn as mg
+    from vit_perception_encoder_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    mg.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    print(f"[bench] device {torch.cuda.get_device_name(0)}; generating 50 layers of seeded inputs", file=sys.stderr,
+          flush=True)
+
+    kinds = wl.tower_layer_kinds()
+    layers = []
+    host_layer3 = None
+    for l in range(wl.N_LAYERS):
+        c = wl.tower_layer(l)
+        if l == 3:
+            host_layer3 = c
+        dq, dk, dv = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (c.q, c.k, c.v))
+        layers.append((dq, dk, dv, [int(x) for x in c.cu_seqlens], c.n_seg, c.flops(), c.meta["kind"]))
+    T = layers[0][0].shape[0]
+    out = torch.empty(T, wl.HEADS * wl.HEAD_DIM, dtype=torch.bfloat16, device=dev)
+    step_flops = sum(x[5] for x in layers)
+
+    def run_step(events=None):
+        for i, (q, k, v, cu, nseg, _, _) in enumerate(layers):
+            if events is not None:
+                events[i][0].record(stream)
+            mg.mgattn_dense(q, k, v, out, cu, nseg, wl.HEADS, wl.HEAD_DIM, wl.SCALE, 0, mg.MGATTN_BF16, stream)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(ev[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per_launch = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(layers))]
+                           for s in range(args.steps)])
+    full_idx = [i for i, x in enumerate(layers) if x[6] == "full"]
+    win_idx = [i for i, x in enumerate(layers) if x[6] == "window"]
+    launch_ms_mean = float(per_launch.mean())
+    flops_per_launch = step_flops / len(layers)
+    achieved = flops_per_launch / (launch_ms_mean * 1e-3) / 1e12
+    full_ms = float(np.median(per_launch[:, full_idx]))
+    win_ms = float(np.median(per_launch[:, win_idx]))
+    full_tf = layers[full_idx[0]][5] / (full_ms * 1e-3) / 1e12
+    win_tf = layers[win_idx[0]][5] / (win_ms * 1e-3) / 1e12
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    hbm = traffic_per_launch()
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": hbm,
+                "kernel": KERNEL_NAME, "launch_ms_mean": launch_ms_mean,
+                "flops_per_launch": flops_per_launch}
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the f64 CPU oracle on one full layer", file=sys.stderr, flush=True)
+        want, cpu = cpu_baseline(host_layer3)
+        q, k, v, cu, nseg, _, _ = layers[3]
+        mg.mgattn_dense(q, k, v, out, cu, nseg, wl.HEADS, wl.HEAD_DIM, wl.SCALE, 0, mg.MGATTN_BF16, stream)
+        torch.cuda.synchronize()
+        got = wl.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).reshape(want.shape)
+        parity = float(np.abs(got - want).max())
+
+    line = {
+        "metric": METRIC,
+        "value": step_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "tower_4096x50: 13 full layers [4096] + 37 window layers [4x1024], H=16, d=96, "
+                               "bf16 N(0,1) seeded per layer, non-causal, scale 1/sqrt(96)",
+                   "tokens": T, "layers": len(layers), "heads": wl.HEADS, "head_dim": wl.HEAD_DIM},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {
+            "tower_ms": ms_per_step,
+            "frac_of_bf16_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "full_layer_4096": {"ms": full_ms, "tflops": full_tf, "frac": full_tf / PEAK_BF16_TFLOPS},
+            "window_layer_4x1024": {"ms": win_ms, "tflops": win_tf, "frac": win_tf / PEAK_BF16_TFLOPS},
+            "step_gflop": step_flops / 1e9,
+            "wall_s_timed_region": wall,
+            "oracle_parity_full_layer_max_abs_err": parity,
+            "kernel_source_sha256": kernel_source_hash(),
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

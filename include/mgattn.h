@@ -1,0 +1,133 @@
+/*
+ * mgattn: segmented multi-head softmax attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the perception-encoder attention of the Muse Glimmer vision
+ * tower as described in vllm.cpp issue #1545 ("Muse Glimmer's vision tower runs 50
+ * layers on the naive attention kernel"):
+ *   - section "Why this one is bad": non-causal, 16 heads, head_dim 96, 50 layers;
+ *   - section "The fix": the block-diagonal window mask is a set of per-segment row
+ *     slices, each attended on its own, and the flash rung honours a causal flag;
+ *   - second comment, "Two of the three labelled uncertainties are now resolved":
+ *     13 full-attention layers (one segment per image) and 37 window layers whose
+ *     segments are 32x32 = 1024-patch windows.
+ * For every segment [a, b) of cu_seqlens, every head h and every query i in [a, b):
+ *     out[i,h,:] = sum_j softmax_j(scale * <q[i,h,:], k[j,h,:]>) * v[j,h,:]
+ * with j over [a, b) (causal: j over [a, i]).
+ *
+ * Refusal conventions follow vllm.cpp PR #1578 ("a model on the naive attention
+ * kernel now says why, and AttentionDenseFlash advertises the head_dim it can
+ * launch"), section "AttentionDenseFlash advertises the head_dim it can launch": the
+ * supported domain and the on-chip memory a launch asks for are pure host queries
+ * that need no GPU, bounds are inclusive, and an unsupported request is refused by
+ * name before any launch instead of surfacing as a bare launch error.
+ *
+ * Every function is callable from C; no C++ type or exception crosses this boundary.
+ */
+#ifndef MGATTN_H
+#define MGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out (one type for all four). */
+typedef enum {
+  MGATTN_F32 = 0,  /* IEEE binary32 */
+  MGATTN_BF16 = 1  /* bfloat16 (upper half of a binary32) */
+} mgattn_dtype;
+
+/* Return codes.  Every negative status means nothing was enqueued. */
+typedef enum {
+  MGATTN_OK = 0,
+  MGATTN_ERR_NULL = -1,      /* a required pointer is NULL */
+  MGATTN_ERR_DTYPE = -2,     /* dtype is not an mgattn_dtype */
+  MGATTN_ERR_HEAD_DIM = -3,  /* head_dim outside mgattn_dense_supported's domain */
+  MGATTN_ERR_HEADS = -4,     /* H < 1 */
+  MGATTN_ERR_SEQLENS = -5,   /* cu_seqlens malformed (see mgattn_dense) */
+  MGATTN_ERR_SEGMENTS = -6,  /* n_seg < 1 */
+  MGATTN_ERR_ALIAS = -7,     /* out overlaps q, k or v */
+  MGATTN_ERR_ALIGN = -8,     /* a tensor pointer is not 16-byte aligned */
+  MGATTN_ERR_SCALE = -9,     /* scale is NaN or infinite, or causal is not 0 or 1 */
+  MGATTN_ERR_LAUNCH = -10,   /* the HIP runtime reported an error for the launch */
+  MGATTN_ERR_DEVICE = -11,   /* the current device is not a gfx950 GPU */
+  MGATTN_ERR_SIZE = -12      /* a segment spans >= 2^31 bytes (len*H*d*element size),
+                                or a launch would need more than 2^31-1 workgroups */
+} mgattn_status;
+
+/*
+ * mgattn_dense: enqueue segmented attention on `stream` and return.
+ *
+ *   q, k, v    device pointers, each [T, H, d] contiguous row-major in `dtype`
+ *              (element (t, h, c) at offset (t*H + h)*d + c), T = cu_seqlens[n_seg].
+ *              Caller-owned; read only.  16-byte aligned.
+ *   out        device pointer, [T, H, d] in `dtype`, caller-owned, written in full
+ *              (every token of every segment, every head).  Must not overlap q, k or v.
+ *              16-byte aligned.
+ *   cu_seqlens HOST pointer to n_seg+1 int32 values: cu_seqlens[0] == 0, non-decreasing,
+ *              cu_seqlens[n_seg] == T > 0.  Segment g is tokens [cu[g], cu[g+1]);
+ *              empty segments are allowed and do nothing.  Read during the call only.
+ *   n_seg      number of segments, >= 1.  No upper limit: large counts are split
+ *              over several launches on the same stream.
+ *   H          heads, >= 1.
+ *   d          head_dim; see mgattn_dense_supported (96 is always supported).
+ *   scale      logit multiplier (for the tower, 1/sqrt(d)); any finite value, 0 included.
+ *   causal     0: every query sees its whole segment.  1: query i sees keys [a, i].
+ *   dtype      an mgattn_dtype.  Accumulation is f32 in both cases; bf16 results are
+ *              rounded to nearest even.
+ *   stream     a hipStream_t (NULL = the default stream).
+ *
+ * Returns MGATTN_OK once the work is enqueued (no host synchronisation), or a
+ * negative mgattn_status.  All argument checks run before anything is enqueued.
+ * MGATTN_ERR_LAUNCH reports an error from the HIP runtime at launch time; errors that
+ * surface later during execution belong to the stream, as for any kernel.
+ * The library allocates no device memory and keeps no pointer after returning; calls
+ * on different streams may overlap.  NaN or infinite input values are not checked:
+ * their rows of out are unspecified.
+ */
+int mgattn_dense(const void* q, const void* k, const void* v, void* out,
+                 const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
+                 int causal, int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char* mgattn_strerror(int status);
+
+/* 1 if (H, d, dtype) can be launched, else 0.  Pure host arithmetic, no GPU needed.
+ * The head_dim domain is {64, 96, 128}; H >= 1; dtype an mgattn_dtype. */
+int mgattn_dense_supported(int H, int d, int dtype);
+
+/* Bytes of LDS (on-chip shared memory) one workgroup of the (d, dtype) kernel asks
+ * for, or a negative mgattn_status if (d, dtype) is not supported.  Pure host
+ * arithmetic, no GPU needed; equals the static LDS footprint of the kernel. */
+long mgattn_dense_lds_bytes(int d, int dtype);
+
+/* Queries per workgroup of the (d, dtype) kernel (the q-tile height), or a negative
+ * mgattn_status.  Pure host arithmetic. */
+int mgattn_dense_block_m(int d, int dtype);
+
+/* Introspection of the work split (pure host arithmetic, no GPU needed).
+ *
+ * mgattn_dense_plan: number of kernel launches mgattn_dense makes for these
+ * arguments (segments are ordered longest first and packed up to 120 per launch),
+ * or a negative mgattn_status.  If grids is not NULL, grids[i] receives the
+ * workgroup count of launch i for i < max_launches.
+ *
+ * mgattn_dense_tile: what workgroup `block` of launch `launch` computes.  Returns 1
+ * and writes {segment index in cu_seqlens, head, first query of the tile relative
+ * to the segment start} to seg_head_q0[0..2]; returns 0 for an idle workgroup; or a
+ * negative mgattn_status.  Every (segment, head, q-tile) of the call appears exactly
+ * once over all launches and blocks. */
+int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
+                      int64_t* grids, int max_launches);
+int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
+                      int launch, int64_t block, int32_t* seg_head_q0);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int mgattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MGATTN_H */

@@ -1,0 +1,167 @@
+"""CPU tests of the C-ABI library: it loads, exports every function include/mgattn.h
+declares, answers its pure host queries, refuses malformed calls by name before
+touching a GPU, and splits work so that every (segment, head, q-tile) is computed
+exactly once.  No compute call is made here (no GPU)."""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+from vit_perception_encoder_amd import mgattn as mg
+
+pytestmark = pytest.mark.cpu
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "mgattn.h"
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mg.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    decls = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(mgattn_[a-z_0-9]+)\s*\(", HEADER.read_text(), re.M))
+    assert decls == set(mg.EXPORTS)
+    for name in decls:
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header(lib):
+    text = HEADER.read_text()
+    for code, name in mg.STATUS_NAMES.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+        s = mg.mgattn_strerror(code)
+        assert s and s != "unknown mgattn status"
+    assert mg.mgattn_strerror(12345) == "unknown mgattn status"
+
+
+def test_supported_domain(lib):
+    for d in (64, 96, 128):
+        for dt in (mg.MGATTN_F32, mg.MGATTN_BF16):
+            assert mg.mgattn_dense_supported(16, d, dt) == 1
+            assert mg.mgattn_dense_supported(1, d, dt) == 1
+    for d in (0, 32, 80, 95, 97, 160, 192, 256):
+        assert mg.mgattn_dense_supported(16, d, mg.MGATTN_BF16) == 0
+    assert mg.mgattn_dense_supported(0, 96, mg.MGATTN_BF16) == 0
+    assert mg.mgattn_dense_supported(16, 96, 2) == 0
+
+
+def test_lds_bytes_arithmetic(lib):
+    """The LDS a workgroup asks for: two stages of a 64-key K tile (pitch d+8) and a
+    transposed V tile (d rows, pitch 72) in bf16; two stages of 32-key K and V tiles
+    (pitch d+4) in f32.  Every supported width fits the 160 KiB of one CU."""
+    for d in (64, 96, 128):
+        want_bf16 = 2 * (64 * (d + 8) + d * (64 + 8)) * 2
+        want_f32 = 2 * 2 * 32 * (d + 4) * 4
+        assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_BF16) == want_bf16
+        assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_F32) == want_f32
+        assert want_bf16 <= 160 * 1024 and want_f32 <= 160 * 1024
+    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 54272
+    assert mg.mgattn_dense_lds_bytes(80, mg.MGATTN_BF16) == -3
+    assert mg.mgattn_dense_lds_bytes(96, 7) == -2
+    assert mg.mgattn_dense_block_m(96, mg.MGATTN_BF16) == 256
+    assert mg.mgattn_dense_block_m(96, mg.MGATTN_F32) == 128
+
+
+# Fake, aligned, non-overlapping "device" addresses: every call below is refused
+# during argument checking, before any HIP call.
+Q, K, V, O = 0x100000, 0x200000, 0x300000, 0x400000
+
+
+def _call(cu, n_seg=None, H=16, d=96, scale=0.1, causal=0, dtype=1, q=Q, k=K, v=V, o=O):
+    return mg.mgattn_dense(q, k, v, o, cu, len(cu) - 1 if n_seg is None else n_seg, H, d, scale,
+                           causal, dtype, None, check=False)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=2), -2),
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1),
+    (dict(n_seg=0), -6),
+    (dict(H=0), -4),
+    (dict(d=80), -3), (dict(d=256), -3),
+    (dict(scale=float("nan")), -9), (dict(scale=float("inf")), -9), (dict(causal=2), -9),
+    (dict(q=Q + 2), -8), (dict(o=O + 8), -8),
+    (dict(o=Q + 16), -7), (dict(o=V - 16), -7),
+])
+def test_refusals(lib, kwargs, status):
+    cu = [0, 64, 64, 200]
+    assert _call(cu, **kwargs) == status
+
+
+@pytest.mark.parametrize("cu", [[1, 10], [0, 10, 5], [0, 0], [0, 0, 0], [0, -5]])
+def test_bad_seqlens(lib, cu):
+    assert _call(cu) == -5
+
+
+def test_null_seqlens(lib):
+    st = lib.mgattn_dense(Q, K, V, O, None, 1, 16, 96, 0.1, 0, 1, None)
+    assert st == -1
+
+
+def test_segment_too_large(lib):
+    # a 2^21-token segment of 16*96 bf16 spans 6 GiB: refused by name
+    assert _call([0, 1 << 21], o=0x10_0000_0000) == -12
+
+
+def _expected_tiles(cu, H, bm):
+    out = set()
+    for g in range(len(cu) - 1):
+        L = cu[g + 1] - cu[g]
+        for h in range(H):
+            for q0 in range(0, L, bm):
+                out.add((g, h, q0))
+    return out
+
+
+@pytest.mark.parametrize("cu,H,dtype,causal", [
+    ([0, 4096], 16, 1, 0),
+    ([0, 1024, 2048, 3072, 4096], 16, 1, 0),
+    ([0, 12288, 16384, 17408], 16, 1, 0),
+    ([0, 1, 1, 300, 557, 557, 1000], 3, 1, 1),
+    ([0, 256], 16, 0, 0),
+    ([0, 100, 357], 8, 0, 1),
+])
+def test_plan_is_a_bijection(lib, cu, H, dtype, causal):
+    bm = mg.mgattn_dense_block_m(96, dtype)
+    grids = mg.mgattn_dense_plan(cu, len(cu) - 1, H, 96, dtype, causal)
+    seen = []
+    for li, grid in enumerate(grids):
+        for b in range(grid):
+            t = mg.mgattn_dense_tile(cu, len(cu) - 1, H, 96, dtype, causal, li, b)
+            assert t is not None
+            seen.append(t)
+            if H % 8 == 0:
+                assert t[1] % 8 == b % 8  # head dealt to XCD b % 8
+    assert len(seen) == len(set(seen))
+    assert set(seen) == _expected_tiles(cu, H, bm)
+
+
+def test_plan_orders_longest_first_and_splits(lib):
+    lens = list(np.random.Generator(np.random.PCG64(5)).integers(0, 700, size=300))
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    grids = mg.mgattn_dense_plan(cu, 300, 16, 96, 1, 0)
+    nonempty = sum(1 for x in lens if x > 0)
+    assert len(grids) == -(-nonempty // 120)
+    assert sum(grids) == 16 * sum(-(-x // 256) for x in lens)
+    # within XCD 0 of the first launch, segment lengths never increase
+    prev = None
+    for b in range(0, grids[0], 8):
+        g, _, _ = mg.mgattn_dense_tile(cu, 300, 16, 96, 1, 0, 0, b)
+        if prev is not None:
+            assert lens[g] <= prev
+        prev = lens[g]
+
+
+def test_plan_causal_puts_last_qtile_first(lib):
+    cu = [0, 1000]
+    first = mg.mgattn_dense_tile(cu, 1, 1, 96, 1, 1, 0, 0)
+    assert first == (0, 0, 768)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError):
+        mg.load_library(tmp_path / "missing.so")

@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 oracle on the same
+seeded inputs.  Tolerances: max |GPU - oracle| <= 2e-2 for bf16 inputs (f32
+accumulation) and <= 1e-4 for f32 inputs.
+
+Small cases are compared element by element over the whole output.  Full-size cases
+(the 50-layer tower at 4096 tokens, the ragged 16k/17k-token batches) run in the
+same launch configuration as the benchmark and are compared on sampled rows the
+oracle computes one by one: every segment's first and last rows, rows on both sides
+of each q-tile edge, and random rows."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from tests.gpu_helpers import BF16_TOL, F32_TOL, run, say
+from vit_perception_encoder_amd import mgattn as mg
+from vit_perception_encoder_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    assert t.cuda.is_available()
+    mg.load_library()
+    return t
+
+
+def _tol(dtype):
+    return BF16_TOL if dtype == wl.BF16 else F32_TOL
+
+
+def _full_check(torch, case: wl.Case, guard_rows=3):
+    say(f"{case.name}: T={case.T} n_seg={case.n_seg} H={case.H} d={case.d} dtype={case.dtype} causal={case.causal}")
+    got, guards = run(torch, case.q, case.k, case.v, case.cu_seqlens, case.H, case.d, case.scale,
+                      case.causal, case.dtype, guard_rows=guard_rows)
+    q, k, v = (x.reshape(case.T, case.H, case.d) for x in (case.q, case.k, case.v))
+    want = orc.attention(q, k, v, case.cu_seqlens, case.H, case.d, case.scale, causal=bool(case.causal))
+    err = np.abs(got - want)
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    assert guards, "kernel wrote outside out"
+    assert np.all(np.isfinite(got))
+    assert err.max() <= _tol(case.dtype), f"max err {err.max():.3e} at (t,h,c)={worst}"
+    return got, want
+
+
+def _sampled_check(torch, case: wl.Case, n_random=256, seed=0):
+    say(f"{case.name} (sampled): T={case.T} n_seg={case.n_seg}")
+    got, guards = run(torch, case.q, case.k, case.v, case.cu_seqlens, case.H, case.d, case.scale,
+                      case.causal, case.dtype, guard_rows=2)
+    assert guards
+    assert np.all(np.isfinite(got))
+    toks, heads = wl.sample_rows(case.cu_seqlens, case.H, n_random, seed)
+    q, k, v = (x.reshape(case.T, case.H, case.d) for x in (case.q, case.k, case.v))
+    want = orc.attention_rows(q, k, v, case.cu_seqlens, case.H, case.d, case.scale, toks, heads,
+                              causal=bool(case.causal))
+    err = np.abs(got[toks, heads] - want)
+    i = int(np.argmax(err.max(axis=1)))
+    assert err.max() <= _tol(case.dtype), f"max err {err.max():.3e} at token {toks[i]} head {heads[i]}"
+    return err.max()
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_config1_tiny_f32(torch):
+    _full_check(torch, wl.config_tiny())
+
+
+def test_config2_full_1024(torch):
+    _full_check(torch, wl.config_full448())
+
+
+def test_config3_window_4x1024(torch):
+    _full_check(torch, wl.config_window896())
+
+
+def test_config4_tower_50_layers(torch):
+    """All 50 layers at 4096 tokens, fresh inputs per layer, sampled rows per layer."""
+    worst = 0.0
+    for layer in range(wl.N_LAYERS):
+        worst = max(worst, _sampled_check(torch, wl.tower_layer(layer), n_random=48, seed=layer))
+    say(f"tower worst sampled error {worst:.3e}")
+
+
+@pytest.mark.parametrize("which", ["5a", "5b"])
+def test_config5_ragged(torch, which):
+    qkv = wl.ragged_inputs(which)
+    for kind in ("full", "window"):
+        _sampled_check(torch, wl.ragged_case(which, kind, qkv), n_random=256, seed=7)
+
+
+# ------------------------------------------------------------------------ edge cases
+
+def _rand_case(name, lens, H=16, d=96, dtype=wl.BF16, causal=0, scale=None, seed=0, qscale=1.0, kscale=1.0):
+    T = int(sum(lens))
+    q = wl.normal_f32(seed, (T, H * d)) * np.float32(qscale)
+    k = wl.normal_f32(seed + 1, (T, H * d)) * np.float32(kscale)
+    v = wl.normal_f32(seed + 2, (T, H * d))
+    if dtype == wl.BF16:
+        q, k, v = (wl.f32_to_bf16_bits(x) for x in (q, k, v))
+    return wl.Case(name, q, k, v, wl.cu_from_lengths(lens), dtype, H=H, d=d,
+                   scale=(1.0 / np.sqrt(d)) if scale is None else scale, causal=causal)
+
+
+RAGGED = [1, 2, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 600]
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_ragged_lengths(torch, dtype, causal):
+    _full_check(torch, _rand_case(f"ragged_{dtype}_{causal}", RAGGED, H=4, dtype=dtype, causal=causal, seed=11))
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_head_dims(torch, d, dtype):
+    _full_check(torch, _rand_case(f"d{d}", [300, 77, 513], H=2, d=d, dtype=dtype, seed=21))
+
+
+@pytest.mark.parametrize("H", [1, 3, 8, 16])
+def test_head_counts(torch, H):
+    _full_check(torch, _rand_case(f"H{H}", [257, 100], H=H, seed=31))
+
+
+def test_empty_segments(torch):
+    _full_check(torch, _rand_case("empties", [0, 40, 0, 0, 300, 0], H=3, seed=41))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.3, 1.7])
+def test_scales(torch, scale):
+    _full_check(torch, _rand_case(f"scale{scale}", [130, 270], H=2, scale=scale, seed=51))
+
+
+def test_many_segments_split_over_launches(torch):
+    lens = np.random.Generator(np.random.PCG64(61)).integers(0, 90, size=300).tolist()
+    case = _rand_case("300_segments", lens, H=2, seed=61)
+    assert len(mg.mgattn_dense_plan(case.cu_seqlens, case.n_seg, 2, 96, wl.BF16)) == 3
+    _full_check(torch, case)
+
+
+def test_large_logits(torch):
+    """Rows scaled by 8 on both Q and K: logits with std ~64, sharp softmax."""
+    _full_check(torch, _rand_case("sharp", [700, 300], H=2, seed=71, qscale=8.0, kscale=8.0))
+
+
+def test_single_key_segments_return_v_exactly(torch):
+    case = _rand_case("single_keys", [1, 1, 5, 1], H=4, seed=81, qscale=4.0, kscale=4.0)
+    got, _ = run(torch, case.q, case.k, case.v, case.cu_seqlens, 4, 96, case.scale, 0, wl.BF16)
+    v = wl.bf16_bits_to_f32(case.v).reshape(case.T, 4, 96).astype(np.float64)
+    for t in (0, 1, 7):
+        assert np.array_equal(got[t], v[t])
+
+
+def test_identical_keys_give_mean_of_v(torch):
+    H, d, lens = 2, 96, [200, 333]
+    case = _rand_case("identical_keys", lens, H=H, seed=91)
+    k = case.k.reshape(case.T, H * d).copy()
+    k[:200] = k[0]
+    k[200:] = k[200]
+    got, _ = run(torch, case.q, k, case.v, case.cu_seqlens, H, d, case.scale, 0, wl.BF16)
+    v = wl.bf16_bits_to_f32(case.v).reshape(case.T, H, d).astype(np.float64)
+    for a, b in ((0, 200), (200, 533)):
+        assert np.abs(got[a:b] - v[a:b].mean(axis=0)).max() <= BF16_TOL
+
+
+def test_key_shift_invariance_stress(torch):
+    """Keys shifted by a large common vector (max-subtraction stress): the GPU still
+    matches the oracle on the same stored keys."""
+    H, d = 2, 96
+    case = _rand_case("shifted", [512, 129], H=H, seed=101)
+    kf = wl.bf16_bits_to_f32(case.k).reshape(case.T, H * d) + wl.normal_f32(102, (1, H * d)) * np.float32(6.0)
+    case.k = wl.f32_to_bf16_bits(kf)
+    _full_check(torch, case)
+
+
+def test_segment_independence_and_determinism(torch):
+    case = wl.config_window896()
+    say("segment independence")
+    got, _ = run(torch, case.q, case.k, case.v, case.cu_seqlens, 16, 96, case.scale, 0, wl.BF16)
+    again, _ = run(torch, case.q, case.k, case.v, case.cu_seqlens, 16, 96, case.scale, 0, wl.BF16)
+    assert np.array_equal(got, again)
+    cu = case.cu_seqlens
+    for g in range(4):
+        a, b = int(cu[g]), int(cu[g + 1])
+        one, _ = run(torch, case.q[a:b], case.k[a:b], case.v[a:b], [0, b - a], 16, 96, case.scale, 0, wl.BF16)
+        assert np.array_equal(one, got[a:b])
+
+
+def test_runtime_refusals_on_device(torch):
+    q = torch.zeros(64 * 1536 + 8, dtype=torch.bfloat16, device="cuda")
+    o = torch.zeros(64 * 1536, dtype=torch.bfloat16, device="cuda")
+    st = mg.mgattn_dense(q[1:], q, q, o, [0, 64], 1, 16, 96, 0.1, 0, wl.BF16, check=False)
+    assert st == -8
+    st = mg.mgattn_dense(q, q, q, q, [0, 64], 1, 16, 96, 0.1, 0, wl.BF16, check=False)
+    assert st == -7
+    with pytest.raises(mg.MgattnError):
+        mg.mgattn_dense(q, q, q, o, [0, 64, 10], 2, 16, 96, 0.1, 0, wl.BF16)

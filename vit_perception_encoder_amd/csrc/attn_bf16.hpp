@@ -1,0 +1,354 @@
+// Single-pass online-softmax attention, bf16 inputs, f32 accumulation, gfx950.
+//
+// What it computes is the segmented softmax attention of the Muse Glimmer vision
+// tower (vllm.cpp issue #1545, sections "Why this one is bad" and "The fix"): each
+// segment of cu_seqlens is attended on its own, non-causal unless asked.  The flash
+// rung the pages route the tower to (PR #1579, "Numerics, both halves") reaches the
+// same function with a running online softmax; this kernel does too, designed for
+// CDNA4 rather than after that CUDA kernel.
+//
+// Layout of the work (one workgroup = 4 waves = one (segment, head, 256-query tile)):
+//   * Each wave owns 64 queries as two 32-query blocks.  Scores are computed
+//     transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
+//     (keys are MFMA rows), Q^T the B operand (queries are MFMA columns).  In the
+//     32x32 accumulator a lane then holds ONE query and 16 of the 32 keys (rows
+//     8*(r/4) + 4*(lane/32) + r%4), so the row max and row sum are in-lane chains
+//     plus a single exchange between lanes l and l^32 (v_permlane32_swap).
+//   * head_dim is the contraction of S^T: D/16 MFMA k-steps (96 = 6 x 16).
+//   * O^T = V^T * P^T, again 32x32x16: V^T is the A operand, P^T the B operand.  A
+//     lane's P^T operand is exactly the 8 probabilities it already holds for one
+//     16-key group, converted to bf16 in place: no cross-lane shuffle of P.  The
+//     matching V^T operand is read from LDS, where V is stored transposed and with
+//     the keys of each 16-key group permuted ([0-3, 8-11 | 4-7, 12-15]) so that
+//     those 8 keys are one contiguous 16-byte read.  O^T is D/32 accumulators of
+//     32x32 (96 = 3 x 32); a lane holds one query's 16 output channels per tile.
+//   * K/V tiles of 64 keys go HBM -> registers -> LDS, double-buffered: the next
+//     tile's global loads are in flight during the current tile's MFMA work, and
+//     one barrier per tile separates the buffers.  LDS rows are padded (K pitch
+//     D+8, V^T pitch 64+8 elements) so every 16-byte MFMA operand read is free of
+//     bank conflicts.
+//   * Softmax uses exp2 with scale*log2(e) folded into one FMA per score.  The
+//     running maximum is refreshed only when a tile's maximum exceeds it by more
+//     than 2^8 in probability terms (decided per wave), so the O rescale is skipped
+//     on almost every tile; this is exact because numerator and denominator share
+//     the same reference maximum.  The row sum adds the bf16-rounded probabilities
+//     that feed the PV product (v_dot2 with ones), so the weights stay normalised.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "plan.hpp"
+
+namespace mgattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct KernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int32_t H;
+  int32_t causal;
+  float c;        // |scale| * log2(e)
+  int32_t negate; // 1 when scale < 0 (Q is negated in registers; exact)
+  SegTable table;
+};
+
+template <int D>
+struct Bf16Tile {
+  static constexpr int kWaves = 4;
+  static constexpr int kQBlocks = 2;                     // 32-query blocks per wave
+  static constexpr int kBlockM = kWaves * kQBlocks * 32; // queries per workgroup
+  static constexpr int kBlockN = 64;                     // keys per LDS tile
+  static constexpr int kKPitch = D + 8;                  // K row pitch (elements)
+  static constexpr int kVPitch = kBlockN + 8;            // V^T row pitch (elements)
+  static constexpr int kKElems = kBlockN * kKPitch;
+  static constexpr int kVElems = D * kVPitch;
+  static constexpr int kStageElems = kKElems + kVElems;
+  static constexpr int kStages = 2;
+  static constexpr int kLdsBytes = kStages * kStageElems * 2;
+  static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head_dim must be a multiple of 32 up to 128");
+  static_assert((kBlockN * D / 8) % (kWaves * 64) == 0, "K tile must split evenly over the threads");
+};
+
+// Exchange with lane l^32 and combine (max or sum) -- one v_permlane32_swap.
+__device__ inline float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Key (relative to the 32-key block) held in accumulator register r by lane half hf.
+__device__ constexpr int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16(KernelArgs a) {
+  using TL = Bf16Tile<D>;
+  constexpr int QB = TL::kQBlocks, BM = TL::kBlockM, BN = TL::kBlockN;
+  constexpr int KS = D / 16;  // MFMA k-steps over head_dim
+  constexpr int CT = D / 32;  // 32-channel output tiles
+  constexpr int KB = BN / 32; // 32-key blocks per LDS tile
+  constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
+  constexpr int NT = TL::kWaves * 64;
+  constexpr int K_CHUNKS = BN * D / 8;           // 16-byte pieces of a K tile
+  constexpr int K_PER_T = K_CHUNKS / NT;
+  constexpr int V_UNITS = (BN / 4) * (D / 8);    // 4 keys x 8 channels each
+  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+  constexpr float kRescaleLog2 = 8.0f;           // refresh the max past 2^8
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
+
+  const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
+  if (!tile.valid) return;
+  const int L = a.table.len[tile.slot];
+  const int q0 = tile.q0;
+  const int H = a.H;
+  const int rs = H * D;  // elements between consecutive tokens
+  const size_t base = (static_cast<size_t>(a.table.start[tile.slot]) * H + tile.head) * D;
+  const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + base;
+  const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + base;
+  const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + base;
+  __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + base;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const float c = a.c;
+
+  // ---- Q fragments (B operand of S^T): lane holds query n, channels 16s + 8hf + [0,8)
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qr = q0 + (wave * QB + qb) * 32 + n;
+    if (qr < L) {
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(qg + static_cast<size_t>(qr) * rs + 8 * hf);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[qb][s] = p[2 * s];
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[qb][s] = bf16x8{};
+    }
+    if (a.negate) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[qb][s] = -qf[qb][s];
+    }
+  }
+
+  const int kend = a.causal ? min(L, q0 + BM) : L;
+  const int ntiles = (kend + BN - 1) / BN;
+
+  // ---- tile staging registers
+  bf16x8 kreg[K_PER_T];
+  bf16x8 vreg[V_PER_T][4];
+
+  auto load_tile = [&](int t) {
+    const int kt0 = t * BN;
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int id = tid + i * NT;
+      const int key = id / (D / 8), part = id % (D / 8);
+      const int row = kt0 + key;
+      kreg[i] = row < L ? *reinterpret_cast<const bf16x8*>(kg + row * rs + part * 8) : bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (V_UNITS % NT == 0 || u < V_UNITS) {
+        const int kq = u % (BN / 4), cg = u / (BN / 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int row = kt0 + 4 * kq + j;
+          vreg[i][j] = row < L ? *reinterpret_cast<const bf16x8*>(vg + row * rs + cg * 8) : bf16x8{};
+        }
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    __bf16* ks = lds + buf * TL::kStageElems;
+    __bf16* vt = ks + TL::kKElems;
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int id = tid + i * NT;
+      const int key = id / (D / 8), part = id % (D / 8);
+      *reinterpret_cast<bf16x8*>(ks + key * KP + part * 8) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int u = tid + i * NT;
+      if (V_UNITS % NT == 0 || u < V_UNITS) {
+        const int kq = u % (BN / 4), cg = u / (BN / 4);
+        // keys 4kq..4kq+3 = 16G + 8a + 4b + [0,4) go to position 16G + 8b + 4a
+        const int pos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+          bf16x4 col = {vreg[i][0][ch], vreg[i][1][ch], vreg[i][2][ch], vreg[i][3][ch]};
+          *reinterpret_cast<bf16x4*>(vt + (cg * 8 + ch) * VP + pos) = col;
+        }
+      }
+    }
+  };
+
+  // ---- running state: lane holds one query per 32-query block
+  f32x16 o[QB][CT];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) o[qb][ct] = f32x16{};
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  // One 32-key block: S^T = K Q^T, softmax update, O^T += V^T P^T.  MASKED is a
+  // compile-time flag so the common (interior) block carries no per-score checks.
+  auto step = [&](auto masked_tag, const __bf16* ks, const __bf16* vt, int kb, int key0, bool first) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    f32x16 s[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + n) * KP + 16 * st + 8 * hf);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][st], s[qb], 0, 0, 0);
+    }
+
+    // keys past the segment end, and (causal) keys after the query, take no weight
+    auto dead = [&](int qb, int r) {
+      const int key = key0 + acc_row(r, hf);
+      return key >= L || (a.causal && key > q0 + (wave * QB + qb) * 32 + n);
+    };
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (dead(qb, r)) s[qb][r] = -INFINITY;
+    }
+
+    // block row max and the (lazy) running-max refresh
+    float m_blk[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = s[qb][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+      m_blk[qb] = half_swap_max(mx);
+    }
+    if (first) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m_run[qb] = m_blk[qb];
+    } else {
+      bool need = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) need |= (m_blk[qb] - m_run[qb]) * c > kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = fmaxf(m_run[qb], m_blk[qb]);
+          const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) o[qb][ct] *= alpha;
+        }
+      }
+    }
+
+    // probabilities -> bf16 B operands of the PV product; row sums of the same values
+    bf16x8 pk[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mc = m_run[qb] * c;
+      float lsum = 0.0f;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h2 + e], c, -mc));
+          if constexpr (MASKED) p = dead(qb, 8 * h2 + e) ? 0.0f : p;
+          pv[e] = static_cast<__bf16>(p);
+        }
+        pk[qb][h2] = pv;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lsum, false);
+      }
+      l_run[qb] += lsum;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8*>(vt + (ct * 32 + n) * VP + kb * 32 + h2 * 16 + 8 * hf);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          o[qb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[qb][h2], o[qb][ct], 0, 0, 0);
+      }
+  };
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const __bf16* ks = lds + buf * TL::kStageElems;
+    const __bf16* vt = ks + TL::kKElems;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int key0 = t * BN + kb * 32;
+      const bool first = (t == 0) && (kb == 0);
+      const bool masked = (key0 + 32 > L) || (a.causal && key0 + 31 > q0 + wave * QB * 32);
+      if (masked)
+        step(std::true_type{}, ks, vt, kb, key0, first);
+      else
+        step(std::false_type{}, ks, vt, kb, key0, first);
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O / l, bf16 (round to nearest even), rows inside the segment only
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float inv = 1.0f / half_swap_sum(l_run[qb]);
+    const int qr = q0 + (wave * QB + qb) * 32 + n;
+    if (qr < L) {
+      __bf16* dst = og + static_cast<size_t>(qr) * rs + 4 * hf;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(o[qb][ct][4 * r4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(dst + ct * 32 + r4 * 8) = val;
+        }
+    }
+  }
+}
+
+}  // namespace mgattn

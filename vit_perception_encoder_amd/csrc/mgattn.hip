@@ -1,0 +1,231 @@
+// C ABI of the mgattn library: argument checks, the launch plan and the launches.
+//
+// Conventions from the pages: the supported domain and the on-chip memory a launch
+// requests are host arithmetic that needs no GPU, bounds are inclusive, and
+// anything unsupported is refused by name before launching (vllm.cpp PR #1578,
+// section "AttentionDenseFlash advertises the head_dim it can launch"); segment
+// boundaries are checked before any slicing or launch (the vision-tower commit of
+// vllm.cpp PR #279, where a coverage check placed after the slicing loop let a
+// mutant hang).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/mgattn.h"
+#include "attn_bf16.hpp"
+#include "attn_f32.hpp"
+#include "plan.hpp"
+
+using namespace mgattn;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool head_dim_ok(int d) { return d == 64 || d == 96 || d == 128; }
+bool dtype_ok(int dt) { return dt == MGATTN_F32 || dt == MGATTN_BF16; }
+size_t elem_size(int dt) { return dt == MGATTN_F32 ? 4 : 2; }
+
+int block_m_of(int d, int dtype) {
+  (void)d;
+  return dtype == MGATTN_BF16 ? Bf16Tile<96>::kBlockM : F32Tile<96>::kBlockM;
+}
+
+long lds_bytes_of(int d, int dtype) {
+  if (dtype == MGATTN_BF16) {
+    switch (d) {
+      case 64: return Bf16Tile<64>::kLdsBytes;
+      case 96: return Bf16Tile<96>::kLdsBytes;
+      case 128: return Bf16Tile<128>::kLdsBytes;
+    }
+  } else {
+    switch (d) {
+      case 64: return F32Tile<64>::kLdsBytes;
+      case 96: return F32Tile<96>::kLdsBytes;
+      case 128: return F32Tile<128>::kLdsBytes;
+    }
+  }
+  return MGATTN_ERR_HEAD_DIM;
+}
+
+static_assert(Bf16Tile<64>::kBlockM == Bf16Tile<128>::kBlockM, "block_m must not depend on d");
+static_assert(F32Tile<64>::kBlockM == F32Tile<128>::kBlockM, "block_m must not depend on d");
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Checks every argument that needs no GPU.  On success, *T_out is the token count.
+int validate(const void* q, const void* k, const void* v, void* out, const int32_t* cu, int n_seg,
+             int H, int d, float scale, int causal, int dtype, int64_t* T_out) {
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  if (!q || !k || !v || !out || !cu) return MGATTN_ERR_NULL;
+  if (n_seg < 1) return MGATTN_ERR_SEGMENTS;
+  if (H < 1) return MGATTN_ERR_HEADS;
+  if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
+  if (!isfinite(scale) || (causal != 0 && causal != 1)) return MGATTN_ERR_SCALE;
+  if (cu[0] != 0) return MGATTN_ERR_SEQLENS;
+  int64_t max_len = 0;
+  for (int g = 0; g < n_seg; ++g) {
+    if (cu[g + 1] < cu[g]) return MGATTN_ERR_SEQLENS;
+    const int64_t len = static_cast<int64_t>(cu[g + 1]) - cu[g];
+    if (len > max_len) max_len = len;
+  }
+  const int64_t T = cu[n_seg];
+  if (T <= 0) return MGATTN_ERR_SEQLENS;
+  // per-segment element offsets are 32-bit inside the kernels
+  if (max_len * static_cast<int64_t>(H) * d * static_cast<int64_t>(elem_size(dtype)) > INT32_MAX)
+    return MGATTN_ERR_SIZE;
+  if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+        reinterpret_cast<uintptr_t>(out)) & 15u) != 0)
+    return MGATTN_ERR_ALIGN;
+  const size_t bytes = static_cast<size_t>(T) * H * d * elem_size(dtype);
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return MGATTN_ERR_ALIAS;
+  *T_out = T;
+  return MGATTN_OK;
+}
+
+// gfx950 check, cached per device ordinal.
+int device_ok() {
+  static int cache[64];  // 0 unknown, 1 yes, 2 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return cache[dev] == 1;
+}
+
+template <typename Kern>
+int launch_all(Kern kern, const std::vector<Launch>& plan, KernelArgs args, hipStream_t stream) {
+  for (const Launch& l : plan) {
+    args.table = l.table;
+    void* params[] = {&args};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(static_cast<unsigned>(l.grid)),
+                                         dim3(256), params, 0, stream);
+    if (e != hipSuccess) return MGATTN_ERR_LAUNCH;
+  }
+  return MGATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mgattn_dense(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,
+                 int n_seg, int H, int d, float scale, int causal, int dtype, void* stream) {
+  int64_t T = 0;
+  const int st = validate(q, k, v, out, cu_seqlens, n_seg, H, d, scale, causal, dtype, &T);
+  if (st != MGATTN_OK) return st;
+  std::vector<Launch> plan;
+  if (!make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
+  if (!device_ok()) return MGATTN_ERR_DEVICE;
+
+  KernelArgs args;
+  memset(&args, 0, sizeof args);
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.o = out;
+  args.H = H;
+  args.causal = causal;
+  args.c = static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);  // log2(e)
+  args.negate = scale < 0.0f ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == MGATTN_BF16) {
+    switch (d) {
+      case 64: return launch_all(attn_fwd_bf16<64>, plan, args, s);
+      case 96: return launch_all(attn_fwd_bf16<96>, plan, args, s);
+      case 128: return launch_all(attn_fwd_bf16<128>, plan, args, s);
+    }
+  } else {
+    switch (d) {
+      case 64: return launch_all(attn_fwd_f32<64>, plan, args, s);
+      case 96: return launch_all(attn_fwd_f32<96>, plan, args, s);
+      case 128: return launch_all(attn_fwd_f32<128>, plan, args, s);
+    }
+  }
+  return MGATTN_ERR_HEAD_DIM;
+}
+
+const char* mgattn_strerror(int status) {
+  switch (status) {
+    case MGATTN_OK: return "ok";
+    case MGATTN_ERR_NULL: return "a required pointer (q, k, v, out or cu_seqlens) is NULL";
+    case MGATTN_ERR_DTYPE: return "dtype is not MGATTN_F32 or MGATTN_BF16";
+    case MGATTN_ERR_HEAD_DIM: return "head_dim not supported (supported: 64, 96, 128)";
+    case MGATTN_ERR_HEADS: return "H must be >= 1";
+    case MGATTN_ERR_SEQLENS:
+      return "cu_seqlens must start at 0, be non-decreasing and end at T > 0";
+    case MGATTN_ERR_SEGMENTS: return "n_seg must be >= 1";
+    case MGATTN_ERR_ALIAS: return "out overlaps q, k or v";
+    case MGATTN_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned";
+    case MGATTN_ERR_SCALE: return "scale must be finite and causal must be 0 or 1";
+    case MGATTN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case MGATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
+    case MGATTN_ERR_SIZE: return "a segment spans more than 2^31 bytes, or the grid is too large";
+  }
+  return "unknown mgattn status";
+}
+
+int mgattn_dense_supported(int H, int d, int dtype) {
+  return (H >= 1 && head_dim_ok(d) && dtype_ok(dtype)) ? 1 : 0;
+}
+
+long mgattn_dense_lds_bytes(int d, int dtype) {
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  return lds_bytes_of(d, dtype);
+}
+
+int mgattn_dense_block_m(int d, int dtype) {
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
+  return block_m_of(d, dtype);
+}
+
+int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
+                      int64_t* grids, int max_launches) {
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  if (!cu_seqlens) return MGATTN_ERR_NULL;
+  if (n_seg < 1) return MGATTN_ERR_SEGMENTS;
+  if (H < 1) return MGATTN_ERR_HEADS;
+  if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
+  if (causal != 0 && causal != 1) return MGATTN_ERR_SCALE;
+  if (cu_seqlens[0] != 0) return MGATTN_ERR_SEQLENS;
+  for (int g = 0; g < n_seg; ++g)
+    if (cu_seqlens[g + 1] < cu_seqlens[g]) return MGATTN_ERR_SEQLENS;
+  if (cu_seqlens[n_seg] <= 0) return MGATTN_ERR_SEQLENS;
+  std::vector<Launch> plan;
+  if (!make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
+  for (int i = 0; i < static_cast<int>(plan.size()) && i < max_launches; ++i)
+    if (grids) grids[i] = plan[i].grid;
+  return static_cast<int>(plan.size());
+}
+
+int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
+                      int launch, int64_t block, int32_t* seg_head_q0) {
+  if (!seg_head_q0) return MGATTN_ERR_NULL;
+  const int nl = mgattn_dense_plan(cu_seqlens, n_seg, H, d, dtype, causal, nullptr, 0);
+  if (nl < 0) return nl;
+  std::vector<Launch> plan;
+  make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan);
+  if (launch < 0 || launch >= nl || block < 0 || block >= plan[launch].grid) return MGATTN_ERR_SIZE;
+  const Tile t = decode_tile(plan[launch].table, H, block_m_of(d, dtype), causal, static_cast<int>(block));
+  if (!t.valid) return 0;
+  seg_head_q0[0] = plan[launch].orig[t.slot];
+  seg_head_q0[1] = t.head;
+  seg_head_q0[2] = t.q0;
+  return 1;
+}
+
+int mgattn_version(void) { return kVersion; }
+
+}  // extern "C"

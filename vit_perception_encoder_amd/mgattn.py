@@ -1,0 +1,154 @@
+"""Thin ctypes binding of the mgattn C ABI (include/mgattn.h), same names as the C side.
+
+Argument marshalling only: every step of the attention runs in the HIP kernels of
+``_lib/libmgattn.so``.  There is no fallback: if the library is missing or the call
+is refused, these functions raise.  Tensors are torch tensors (device memory and
+streams come from PyTorch); a raw integer device address is accepted as well.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+from typing import Sequence
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "_lib" / "libmgattn.so"
+
+MGATTN_F32 = 0
+MGATTN_BF16 = 1
+
+STATUS_NAMES = {
+    0: "MGATTN_OK", -1: "MGATTN_ERR_NULL", -2: "MGATTN_ERR_DTYPE", -3: "MGATTN_ERR_HEAD_DIM",
+    -4: "MGATTN_ERR_HEADS", -5: "MGATTN_ERR_SEQLENS", -6: "MGATTN_ERR_SEGMENTS",
+    -7: "MGATTN_ERR_ALIAS", -8: "MGATTN_ERR_ALIGN", -9: "MGATTN_ERR_SCALE",
+    -10: "MGATTN_ERR_LAUNCH", -11: "MGATTN_ERR_DEVICE", -12: "MGATTN_ERR_SIZE",
+}
+
+EXPORTS = ["mgattn_dense", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
+           "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_version"]
+
+
+class MgattnError(RuntimeError):
+    def __init__(self, status: int, what: str = "mgattn_dense"):
+        self.status = status
+        super().__init__(f"{what} failed: {STATUS_NAMES.get(status, status)}: {mgattn_strerror(status)}")
+
+
+_lib = None
+
+
+def load_library(path: str | os.PathLike | None = None):
+    """Load libmgattn.so (built by ``python -m vit_perception_encoder_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise ImportError(f"mgattn HIP library not built: {p} is missing "
+                          "(run `python -m vit_perception_encoder_amd.build`)")
+    lib = ctypes.CDLL(str(p))
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.mgattn_dense.restype = i32
+    lib.mgattn_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp]
+    lib.mgattn_strerror.restype = ctypes.c_char_p
+    lib.mgattn_strerror.argtypes = [i32]
+    lib.mgattn_dense_supported.restype = i32
+    lib.mgattn_dense_supported.argtypes = [i32, i32, i32]
+    lib.mgattn_dense_lds_bytes.restype = ctypes.c_long
+    lib.mgattn_dense_lds_bytes.argtypes = [i32, i32]
+    lib.mgattn_dense_block_m.restype = i32
+    lib.mgattn_dense_block_m.argtypes = [i32, i32]
+    lib.mgattn_dense_plan.restype = i32
+    lib.mgattn_dense_plan.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32]
+    lib.mgattn_dense_tile.restype = i32
+    lib.mgattn_dense_tile.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, vp]
+    lib.mgattn_version.restype = i32
+    lib.mgattn_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return 0
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _cu_array(cu_seqlens):
+    seq = [int(x) for x in cu_seqlens]
+    return (ctypes.c_int32 * len(seq))(*seq), len(seq)
+
+
+def mgattn_dense(q, k, v, out, cu_seqlens: Sequence[int], n_seg: int, H: int, d: int, scale: float,
+                 causal: int, dtype: int, stream=None, check: bool = True) -> int:
+    """Enqueue segmented attention (see mgattn_dense in include/mgattn.h).
+
+    ``cu_seqlens`` is a host sequence of n_seg+1 ints.  Returns the status; with
+    ``check`` (the default) a negative status raises MgattnError instead."""
+    lib = load_library()
+    cu, ncu = _cu_array(cu_seqlens)
+    if ncu < n_seg + 1:
+        raise ValueError(f"cu_seqlens has {ncu} entries, n_seg={n_seg} needs {n_seg + 1}")
+    st = lib.mgattn_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.cast(cu, ctypes.c_void_p), int(n_seg),
+                          int(H), int(d), float(scale), int(causal), int(dtype), _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st)
+    return st
+
+
+def mgattn_strerror(status: int) -> str:
+    return load_library().mgattn_strerror(int(status)).decode()
+
+
+def mgattn_dense_supported(H: int, d: int, dtype: int) -> int:
+    return load_library().mgattn_dense_supported(int(H), int(d), int(dtype))
+
+
+def mgattn_dense_lds_bytes(d: int, dtype: int) -> int:
+    return load_library().mgattn_dense_lds_bytes(int(d), int(dtype))
+
+
+def mgattn_dense_block_m(d: int, dtype: int) -> int:
+    return load_library().mgattn_dense_block_m(int(d), int(dtype))
+
+
+def mgattn_dense_plan(cu_seqlens, n_seg: int, H: int, d: int, dtype: int, causal: int = 0) -> list[int]:
+    """Workgroup count of each launch mgattn_dense would make (raises on refusal)."""
+    lib = load_library()
+    cu, _ = _cu_array(cu_seqlens)
+    n = lib.mgattn_dense_plan(ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), int(dtype),
+                              int(causal), None, 0)
+    if n < 0:
+        raise MgattnError(n, "mgattn_dense_plan")
+    grids = (ctypes.c_int64 * max(n, 1))()
+    lib.mgattn_dense_plan(ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), int(dtype),
+                          int(causal), ctypes.cast(grids, ctypes.c_void_p), n)
+    return [int(g) for g in grids[:n]]
+
+
+def mgattn_dense_tile(cu_seqlens, n_seg: int, H: int, d: int, dtype: int, causal: int, launch: int, block: int):
+    """(segment, head, q0) computed by one workgroup, or None for an idle one."""
+    lib = load_library()
+    cu, _ = _cu_array(cu_seqlens)
+    out = (ctypes.c_int32 * 3)()
+    r = lib.mgattn_dense_tile(ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), int(dtype),
+                              int(causal), int(launch), int(block), ctypes.cast(out, ctypes.c_void_p))
+    if r < 0:
+        raise MgattnError(r, "mgattn_dense_tile")
+    return (int(out[0]), int(out[1]), int(out[2])) if r == 1 else None
+
+
+def mgattn_version() -> int:
+    return load_library().mgattn_version()
