@@ -8,12 +8,17 @@ f32 accumulation, fresh seeded N(0,1) Q/K/V per layer, all resident in HBM befor
 timing.  Layer kinds follow vllm.cpp issue #1545, second comment ("Two of the three
 labelled uncertainties are now resolved").
 
-Prints ONE JSON line: algorithmic TFLOP/s over the whole step (4*S^2*d*H per
-segment), ms per step (= ms per tower), the roofline of the attention kernel (HIP
-events around each launch on the launch stream), and the f64 CPU oracle timed on a
-bounded sample of the same workload on this host.
+The 50 launches of a step are captured once into a HIP graph and replayed (--eager
+launches them from Python instead).  HIP events on the launch stream bracket the K
+timed steps; every launch inside is the attention kernel, so its average launch
+duration is the bracketed time over the launches.  A separate eager pass with events
+around each launch gives the full-layer / window-layer breakdown.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--copy-calibration]
+Prints ONE JSON line: algorithmic TFLOP/s over the whole step (4*S^2*d*H per
+segment), ms per step (= ms per tower), the roofline of the attention kernel, and
+the f64 CPU oracle timed on a bounded sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--eager] [--no-cpu-baseline] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -86,6 +91,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch the 50 layers eagerly instead of replaying a graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -119,39 +125,68 @@ def main() -> int:
     out = torch.empty(T, wl.HEADS * wl.HEAD_DIM, dtype=torch.bfloat16, device=dev)
     step_flops = sum(x[5] for x in layers)
 
-    def run_step(events=None):
+    def run_step(strm, events=None):
         for i, (q, k, v, cu, nseg, _, _) in enumerate(layers):
             if events is not None:
-                events[i][0].record(stream)
-            mg.mgattn_dense(q, k, v, out, cu, nseg, wl.HEADS, wl.HEAD_DIM, wl.SCALE, 0, mg.MGATTN_BF16, stream)
+                events[i][0].record(strm)
+            mg.mgattn_dense(q, k, v, out, cu, nseg, wl.HEADS, wl.HEAD_DIM, wl.SCALE, 0, mg.MGATTN_BF16, strm)
             if events is not None:
-                events[i][1].record(stream)
+                events[i][1].record(strm)
 
     for _ in range(args.warmup):
-        run_step()
+        run_step(stream)
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
 
-    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers] for _ in range(args.steps)]
+    graph = None
+    if not args.eager:
+        # The 50 launches of one step are captured once and replayed: no host launch
+        # overhead between layers.
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run_step(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps, {'eager' if graph is None else 'graph'}); "
+          f"timing {args.steps} steps", file=sys.stderr, flush=True)
+
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for s in range(args.steps):
-        run_step(ev[s])
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(stream)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
-
-    per_launch = np.array([[ev[s][i][0].elapsed_time(ev[s][i][1]) for i in range(len(layers))]
-                           for s in range(args.steps)])
-    full_idx = [i for i, x in enumerate(layers) if x[6] == "full"]
-    win_idx = [i for i, x in enumerate(layers) if x[6] == "window"]
-    launch_ms_mean = float(per_launch.mean())
+    # every launch in the timed region is the attention kernel: its average launch
+    # duration is the region's time over the launches (gaps between launches included)
+    launch_ms_mean = ms_per_step / len(layers)
     flops_per_launch = step_flops / len(layers)
     achieved = flops_per_launch / (launch_ms_mean * 1e-3) / 1e12
+
+    # per-layer-kind breakdown: a separate eager pass with events around each launch
+    nb = max(3, min(args.steps, 10))
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers] for _ in range(nb)]
+    for s_ in range(nb):
+        run_step(stream, ev[s_])
+    torch.cuda.synchronize()
+    per_launch = np.array([[ev[s_][i][0].elapsed_time(ev[s_][i][1]) for i in range(len(layers))]
+                           for s_ in range(nb)])
+    full_idx = [i for i, x in enumerate(layers) if x[6] == "full"]
+    win_idx = [i for i, x in enumerate(layers) if x[6] == "window"]
     full_ms = float(np.median(per_launch[:, full_idx]))
     win_ms = float(np.median(per_launch[:, win_idx]))
     full_tf = layers[full_idx[0]][5] / (full_ms * 1e-3) / 1e12
@@ -194,6 +229,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "launch": "eager" if graph is None else "hip_graph",
         "config": {"workload": "tower_4096x50: 13 full layers [4096] + 37 window layers [4x1024], H=16, d=96, "
                                "bf16 N(0,1) seeded per layer, non-causal, scale 1/sqrt(96)",
                    "tokens": T, "layers": len(layers), "heads": wl.HEADS, "head_dim": wl.HEAD_DIM},

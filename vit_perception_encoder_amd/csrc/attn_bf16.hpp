@@ -7,8 +7,9 @@
 // same function with a running online softmax; this kernel does too, designed for
 // CDNA4 rather than after that CUDA kernel.
 //
-// Layout of the work (one workgroup = 4 waves = one (segment, head, 256-query tile)):
-//   * Each wave owns 64 queries as two 32-query blocks.  Scores are computed
+// Layout of the work (one workgroup = 8 waves = one (segment, head, 256-query tile);
+// two waves share each SIMD, so one wave's softmax overlaps the other's MFMAs):
+//   * Each wave owns 32 queries (one 32-query block).  Scores are computed
 //     transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
 //     (keys are MFMA rows), Q^T the B operand (queries are MFMA columns).  In the
 //     32x32 accumulator a lane then holds ONE query and 16 of the 32 keys (rows
@@ -22,11 +23,12 @@
 //     the keys of each 16-key group permuted ([0-3, 8-11 | 4-7, 12-15]) so that
 //     those 8 keys are one contiguous 16-byte read.  O^T is D/32 accumulators of
 //     32x32 (96 = 3 x 32); a lane holds one query's 16 output channels per tile.
-//   * K/V tiles of 64 keys go HBM -> registers -> LDS, double-buffered: the next
+//   * K/V tiles of 128 keys go HBM -> registers -> LDS, double-buffered: the next
 //     tile's global loads are in flight during the current tile's MFMA work, and
 //     one barrier per tile separates the buffers.  LDS rows are padded (K pitch
-//     D+8, V^T pitch 64+8 elements) so every 16-byte MFMA operand read is free of
-//     bank conflicts.
+//     D+8, V^T pitch 128+8 elements) so every 16-byte MFMA operand read is free of
+//     bank conflicts.  The softmax runs on 64-key steps (two 32-key blocks) to
+//     amortise the per-step row reduction.
 //   * Softmax uses exp2 with scale*log2(e) folded into one FMA per score.  The
 //     running maximum is refreshed only when a tile's maximum exceeds it by more
 //     than 2^8 in probability terms (decided per wave), so the O rescale is skipped
@@ -64,10 +66,12 @@ struct KernelArgs {
 
 template <int D>
 struct Bf16Tile {
-  static constexpr int kWaves = 4;
-  static constexpr int kQBlocks = 2;                     // 32-query blocks per wave
+  static constexpr int kWaves = 8;
+  static constexpr int kQBlocks = 1;                     // 32-query blocks per wave
   static constexpr int kBlockM = kWaves * kQBlocks * 32; // queries per workgroup
-  static constexpr int kBlockN = 64;                     // keys per LDS tile
+  static constexpr int kBlockN = 128;                    // keys per LDS tile
+  static constexpr int kStepBlocks = 2;                  // 32-key blocks per softmax step
+  static constexpr int kThreads = kWaves * 64;
   static constexpr int kKPitch = D + 8;                  // K row pitch (elements)
   static constexpr int kVPitch = kBlockN + 8;            // V^T row pitch (elements)
   static constexpr int kKElems = kBlockN * kKPitch;
@@ -76,7 +80,7 @@ struct Bf16Tile {
   static constexpr int kStages = 2;
   static constexpr int kLdsBytes = kStages * kStageElems * 2;
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head_dim must be a multiple of 32 up to 128");
-  static_assert((kBlockN * D / 8) % (kWaves * 64) == 0, "K tile must split evenly over the threads");
+  static_assert(kBlockN % (32 * kStepBlocks) == 0, "LDS tile must hold whole softmax steps");
 };
 
 // Exchange with lane l^32 and combine (max or sum) -- one v_permlane32_swap.
@@ -93,17 +97,18 @@ __device__ inline float half_swap_sum(float x) {
 __device__ constexpr int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
 template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(KernelArgs a) {
   using TL = Bf16Tile<D>;
   constexpr int QB = TL::kQBlocks, BM = TL::kBlockM, BN = TL::kBlockN;
   constexpr int KS = D / 16;  // MFMA k-steps over head_dim
   constexpr int CT = D / 32;  // 32-channel output tiles
-  constexpr int KB = BN / 32; // 32-key blocks per LDS tile
+  constexpr int SB = TL::kStepBlocks;
+  constexpr int NSTEP = BN / (32 * SB);  // softmax steps per LDS tile
   constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
-  constexpr int NT = TL::kWaves * 64;
+  constexpr int NT = TL::kThreads;
   constexpr int K_CHUNKS = BN * D / 8;           // 16-byte pieces of a K tile
-  constexpr int K_PER_T = K_CHUNKS / NT;
+  constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
   constexpr int V_UNITS = (BN / 4) * (D / 8);    // 4 keys x 8 channels each
   constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
   constexpr float kRescaleLog2 = 8.0f;           // refresh the max past 2^8
@@ -160,9 +165,11 @@ void attn_fwd_bf16(KernelArgs a) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int id = tid + i * NT;
-      const int key = id / (D / 8), part = id % (D / 8);
-      const int row = kt0 + key;
-      kreg[i] = row < L ? *reinterpret_cast<const bf16x8*>(kg + row * rs + part * 8) : bf16x8{};
+      if (K_CHUNKS % NT == 0 || id < K_CHUNKS) {
+        const int key = id / (D / 8), part = id % (D / 8);
+        const int row = kt0 + key;
+        kreg[i] = row < L ? *reinterpret_cast<const bf16x8*>(kg + row * rs + part * 8) : bf16x8{};
+      }
     }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
@@ -184,8 +191,10 @@ void attn_fwd_bf16(KernelArgs a) {
 #pragma unroll
     for (int i = 0; i < K_PER_T; ++i) {
       const int id = tid + i * NT;
-      const int key = id / (D / 8), part = id % (D / 8);
-      *reinterpret_cast<bf16x8*>(ks + key * KP + part * 8) = kreg[i];
+      if (K_CHUNKS % NT == 0 || id < K_CHUNKS) {
+        const int key = id / (D / 8), part = id % (D / 8);
+        *reinterpret_cast<bf16x8*>(ks + key * KP + part * 8) = kreg[i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < V_PER_T; ++i) {
@@ -219,41 +228,51 @@ void attn_fwd_bf16(KernelArgs a) {
 
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // One 32-key block: S^T = K Q^T, softmax update, O^T += V^T P^T.  MASKED is a
-  // compile-time flag so the common (interior) block carries no per-score checks.
-  auto step = [&](auto masked_tag, const __bf16* ks, const __bf16* vt, int kb, int key0, bool first) {
+  // One softmax step over SB blocks of 32 keys: S^T = K Q^T, online-softmax update,
+  // O^T += V^T P^T.  MASKED is a compile-time flag so interior steps carry no
+  // per-score checks.
+  auto step = [&](auto masked_tag, const __bf16* ks, const __bf16* vt, int kb0, int key0, bool first) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[QB];
+    f32x16 s[QB][SB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int st = 0; st < KS; ++st) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (kb * 32 + n) * KP + 16 * st + 8 * hf);
+      for (int b = 0; b < SB; ++b) s[qb][b] = f32x16{};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][st], s[qb], 0, 0, 0);
-    }
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int b = 0; b < SB; ++b) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][st], s[qb][b], 0, 0, 0);
+      }
 
     // keys past the segment end, and (causal) keys after the query, take no weight
-    auto dead = [&](int qb, int r) {
-      const int key = key0 + acc_row(r, hf);
+    auto dead = [&](int qb, int b, int r) {
+      const int key = key0 + b * 32 + acc_row(r, hf);
       return key >= L || (a.causal && key > q0 + (wave * QB + qb) * 32 + n);
     };
     if constexpr (MASKED) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (dead(qb, r)) s[qb][r] = -INFINITY;
+        for (int b = 0; b < SB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (dead(qb, b, r)) s[qb][b][r] = -INFINITY;
     }
 
-    // block row max and the (lazy) running-max refresh
+    // step row max and the (lazy) running-max refresh
     float m_blk[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0];
+      float mx = s[qb][0][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qb][r]);
+      for (int b = 0; b < SB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][b][r]);
       m_blk[qb] = half_swap_max(mx);
     }
     if (first) {
@@ -277,39 +296,43 @@ void attn_fwd_bf16(KernelArgs a) {
     }
 
     // probabilities -> bf16 B operands of the PV product; row sums of the same values
-    bf16x8 pk[QB][2];
+    bf16x8 pk[QB][SB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float mc = m_run[qb] * c;
       float lsum = 0.0f;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 pv;
+      for (int b = 0; b < SB; ++b)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * h2 + e], c, -mc));
-          if constexpr (MASKED) p = dead(qb, 8 * h2 + e) ? 0.0f : p;
-          pv[e] = static_cast<__bf16>(p);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 pv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + e], c, -mc));
+            if constexpr (MASKED) p = dead(qb, b, 8 * h2 + e) ? 0.0f : p;
+            pv[e] = static_cast<__bf16>(p);
+          }
+          pk[qb][b][h2] = pv;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lsum, false);
         }
-        pk[qb][h2] = pv;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lsum, false);
-      }
       l_run[qb] += lsum;
     }
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int b = 0; b < SB; ++b)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(vt + (ct * 32 + n) * VP + kb * 32 + h2 * 16 + 8 * hf);
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          o[qb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[qb][h2], o[qb][ct], 0, 0, 0);
-      }
+        for (int ct = 0; ct < CT; ++ct) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (ct * 32 + n) * VP + (kb0 + b) * 32 +
+                                                             h2 * 16 + 8 * hf);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[qb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[qb][b][h2], o[qb][ct], 0, 0, 0);
+        }
   };
 
   for (int t = 0; t < ntiles; ++t) {
@@ -318,14 +341,15 @@ void attn_fwd_bf16(KernelArgs a) {
     const __bf16* ks = lds + buf * TL::kStageElems;
     const __bf16* vt = ks + TL::kKElems;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int key0 = t * BN + kb * 32;
-      const bool first = (t == 0) && (kb == 0);
-      const bool masked = (key0 + 32 > L) || (a.causal && key0 + 31 > q0 + wave * QB * 32);
+    for (int j = 0; j < NSTEP; ++j) {
+      const int key0 = t * BN + j * SB * 32;
+      if (key0 >= kend) break;  // workgroup-uniform: the tile's remaining keys are all past the end
+      const bool first = (t == 0) && (j == 0);
+      const bool masked = (key0 + SB * 32 > L) || (a.causal && key0 + SB * 32 - 1 > q0 + wave * QB * 32);
       if (masked)
-        step(std::true_type{}, ks, vt, kb, key0, first);
+        step(std::true_type{}, ks, vt, j * SB, key0, first);
       else
-        step(std::false_type{}, ks, vt, kb, key0, first);
+        step(std::false_type{}, ks, vt, j * SB, key0, first);
     }
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();

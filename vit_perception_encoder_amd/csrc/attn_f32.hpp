@@ -23,6 +23,7 @@ template <int D>
 struct F32Tile {
   static constexpr int kWaves = 4;
   static constexpr int kBlockM = kWaves * 32;  // one 32-query block per wave
+  static constexpr int kThreads = kWaves * 64;
   static constexpr int kBlockN = 32;           // keys per LDS tile
   static constexpr int kPitch = D + 4;         // K and V row pitch (floats)
   static constexpr int kTileElems = kBlockN * kPitch;

@@ -105,12 +105,12 @@ int device_ok() {
 }
 
 template <typename Kern>
-int launch_all(Kern kern, const std::vector<Launch>& plan, KernelArgs args, hipStream_t stream) {
+int launch_all(Kern kern, int threads, const std::vector<Launch>& plan, KernelArgs args, hipStream_t stream) {
   for (const Launch& l : plan) {
     args.table = l.table;
     void* params[] = {&args};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(static_cast<unsigned>(l.grid)),
-                                         dim3(256), params, 0, stream);
+                                         dim3(threads), params, 0, stream);
     if (e != hipSuccess) return MGATTN_ERR_LAUNCH;
   }
   return MGATTN_OK;
@@ -142,15 +142,15 @@ int mgattn_dense(const void* q, const void* k, const void* v, void* out, const i
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MGATTN_BF16) {
     switch (d) {
-      case 64: return launch_all(attn_fwd_bf16<64>, plan, args, s);
-      case 96: return launch_all(attn_fwd_bf16<96>, plan, args, s);
-      case 128: return launch_all(attn_fwd_bf16<128>, plan, args, s);
+      case 64: return launch_all(attn_fwd_bf16<64>, Bf16Tile<64>::kThreads, plan, args, s);
+      case 96: return launch_all(attn_fwd_bf16<96>, Bf16Tile<96>::kThreads, plan, args, s);
+      case 128: return launch_all(attn_fwd_bf16<128>, Bf16Tile<128>::kThreads, plan, args, s);
     }
   } else {
     switch (d) {
-      case 64: return launch_all(attn_fwd_f32<64>, plan, args, s);
-      case 96: return launch_all(attn_fwd_f32<96>, plan, args, s);
-      case 128: return launch_all(attn_fwd_f32<128>, plan, args, s);
+      case 64: return launch_all(attn_fwd_f32<64>, F32Tile<64>::kThreads, plan, args, s);
+      case 96: return launch_all(attn_fwd_f32<96>, F32Tile<96>::kThreads, plan, args, s);
+      case 128: return launch_all(attn_fwd_f32<128>, F32Tile<128>::kThreads, plan, args, s);
     }
   }
   return MGATTN_ERR_HEAD_DIM;
