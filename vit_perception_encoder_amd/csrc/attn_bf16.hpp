@@ -27,14 +27,15 @@
 //     tile's global loads are in flight during the current tile's MFMA work, and
 //     one barrier per tile separates the buffers.  LDS rows are padded (K pitch
 //     D+8, V^T pitch 128+8 elements) so every 16-byte MFMA operand read is free of
-//     bank conflicts.  The softmax runs on 64-key steps (two 32-key blocks) to
-//     amortise the per-step row reduction.
-//   * Softmax uses exp2 with scale*log2(e) folded into one FMA per score.  The
-//     running maximum is refreshed only when a tile's maximum exceeds it by more
-//     than 2^8 in probability terms (decided per wave), so the O rescale is skipped
-//     on almost every tile; this is exact because numerator and denominator share
-//     the same reference maximum.  The row sum adds the bf16-rounded probabilities
-//     that feed the PV product (v_dot2 with ones), so the weights stay normalised.
+//     bank conflicts.  A tile is two softmax steps of 64 keys (32 scores per lane).
+//   * Softmax uses exp2 with scale*log2(e) folded into one FMA per score, against a
+//     reference maximum per query: the first tile's row maximum.  Later tiles do not
+//     recompute the maximum.  Exactness does not depend on the reference (numerator
+//     and denominator share it); only range does, so a tile whose partial row sum
+//     exceeds 2^64 (or is not finite) is redone after refreshing the reference to
+//     the true maximum and rescaling O and the row sum (a rare, wave-uniform path).
+//   * The row sum adds the bf16-rounded probabilities that feed the PV product
+//     (v_dot2 with ones), so the weights stay normalised.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,7 +71,7 @@ struct Bf16Tile {
   static constexpr int kQBlocks = 1;                     // 32-query blocks per wave
   static constexpr int kBlockM = kWaves * kQBlocks * 32; // queries per workgroup
   static constexpr int kBlockN = 128;                    // keys per LDS tile
-  static constexpr int kStepBlocks = 2;                  // 32-key blocks per softmax step
+  static constexpr int kStepKeys = 64;                   // keys per softmax step
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kKPitch = D + 8;                  // K row pitch (elements)
   static constexpr int kVPitch = kBlockN + 8;            // V^T row pitch (elements)
@@ -80,7 +81,7 @@ struct Bf16Tile {
   static constexpr int kStages = 2;
   static constexpr int kLdsBytes = kStages * kStageElems * 2;
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head_dim must be a multiple of 32 up to 128");
-  static_assert(kBlockN % (32 * kStepBlocks) == 0, "LDS tile must hold whole softmax steps");
+  static_assert(kBlockN % kStepKeys == 0 && kStepKeys % 32 == 0, "LDS tile must hold whole softmax steps");
 };
 
 // Exchange with lane l^32 and combine (max or sum) -- one v_permlane32_swap.
@@ -96,22 +97,37 @@ __device__ inline float half_swap_sum(float x) {
 // Key (relative to the 32-key block) held in accumulator register r by lane half hf.
 __device__ constexpr int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
+// In-place v *= a on every element.  The tied register operand keeps the scaled
+// accumulator in the registers it already occupies, so the (rare) rescale branch
+// does not force the compiler to copy the accumulators at the branch join.
+__device__ inline void scale_in_place(f32x16& v, float a) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float t = v[i];
+    asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t) : "v"(a));
+    v[i] = t;
+  }
+}
+
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(KernelArgs a) {
   using TL = Bf16Tile<D>;
-  constexpr int QB = TL::kQBlocks, BM = TL::kBlockM, BN = TL::kBlockN;
-  constexpr int KS = D / 16;  // MFMA k-steps over head_dim
-  constexpr int CT = D / 32;  // 32-channel output tiles
-  constexpr int SB = TL::kStepBlocks;
-  constexpr int NSTEP = BN / (32 * SB);  // softmax steps per LDS tile
+  constexpr int BM = TL::kBlockM, BN = TL::kBlockN;
+  constexpr int KS = D / 16;   // MFMA k-steps over head_dim
+  constexpr int CT = D / 32;   // 32-channel output tiles
+  constexpr int NB = TL::kStepKeys / 32;  // 32-key blocks per softmax step
+  constexpr int NSTEP = BN / TL::kStepKeys;  // softmax steps per LDS tile
   constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
   constexpr int NT = TL::kThreads;
-  constexpr int K_CHUNKS = BN * D / 8;           // 16-byte pieces of a K tile
+  constexpr int K_CHUNKS = BN * D / 8;         // 16-byte pieces of a K tile
   constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-  constexpr int V_UNITS = (BN / 4) * (D / 8);    // 4 keys x 8 channels each
+  constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 channels each
   constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
-  constexpr float kRescaleLog2 = 8.0f;           // refresh the max past 2^8
+  // A row's partial sum over one tile above 2^64 means the reference maximum is stale
+  // by a wide margin: the tile is redone against a refreshed maximum.
+  constexpr float kSumLimit = 18446744073709551616.0f;
+  static_assert(TL::kQBlocks == 1, "one 32-query block per wave");
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
 
@@ -119,9 +135,8 @@ void attn_fwd_bf16(KernelArgs a) {
   if (!tile.valid) return;
   const int L = a.table.len[tile.slot];
   const int q0 = tile.q0;
-  const int H = a.H;
-  const int rs = H * D;  // elements between consecutive tokens
-  const size_t base = (static_cast<size_t>(a.table.start[tile.slot]) * H + tile.head) * D;
+  const int rs = a.H * D;  // elements between consecutive tokens
+  const size_t base = (static_cast<size_t>(a.table.start[tile.slot]) * a.H + tile.head) * D;
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + base;
   const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + base;
   const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + base;
@@ -133,55 +148,75 @@ void attn_fwd_bf16(KernelArgs a) {
   const int n = lane & 31;
   const int hf = lane >> 5;
   const float c = a.c;
+  const int qr = q0 + wave * 32 + n;  // this lane's query (relative to the segment)
+  const int qmin = q0 + wave * 32;    // the wave's first query
 
-  // ---- Q fragments (B operand of S^T): lane holds query n, channels 16s + 8hf + [0,8)
-  bf16x8 qf[QB][KS];
+  // ---- Q fragments (B operand of S^T): lane holds query qr, channels 16s + 8hf + [0,8)
+  bf16x8 qf[KS];
+  if (qr < L) {
+    const bf16x8* p = reinterpret_cast<const bf16x8*>(qg + static_cast<size_t>(qr) * rs + 8 * hf);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qr = q0 + (wave * QB + qb) * 32 + n;
-    if (qr < L) {
-      const bf16x8* p = reinterpret_cast<const bf16x8*>(qg + static_cast<size_t>(qr) * rs + 8 * hf);
+    for (int s = 0; s < KS; ++s) qf[s] = p[2 * s];
+  } else {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[qb][s] = p[2 * s];
-    } else {
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  if (a.negate) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[qb][s] = bf16x8{};
-    }
-    if (a.negate) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[qb][s] = -qf[qb][s];
-    }
+    for (int s = 0; s < KS; ++s) qf[s] = -qf[s];
   }
 
   const int kend = a.causal ? min(L, q0 + BM) : L;
   const int ntiles = (kend + BN - 1) / BN;
 
-  // ---- tile staging registers
+  // ---- tile staging: per-thread offsets are fixed, a tile only moves the base
+  int k_row[K_PER_T], k_goff[K_PER_T], k_loff[K_PER_T];
+#pragma unroll
+  for (int i = 0; i < K_PER_T; ++i) {
+    const int id = tid + i * NT;
+    const int key = id / (D / 8), part = id % (D / 8);
+    k_row[i] = (K_CHUNKS % NT == 0 || id < K_CHUNKS) ? key : BN;  // BN: never loaded
+    k_goff[i] = key * rs + part * 8;
+    k_loff[i] = key * KP + part * 8;
+  }
+  int v_row[V_PER_T], v_goff[V_PER_T], v_loff[V_PER_T];
+#pragma unroll
+  for (int i = 0; i < V_PER_T; ++i) {
+    const int u = tid + i * NT;
+    const int kq = u % (BN / 4), cg = u / (BN / 4);
+    // keys 4kq..4kq+3 = 16G + 8a + 4b + [0,4) go to position 16G + 8b + 4a of each V^T row
+    const int pos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+    v_row[i] = (V_UNITS % NT == 0 || u < V_UNITS) ? 4 * kq : BN;
+    v_goff[i] = 4 * kq * rs + cg * 8;
+    v_loff[i] = cg * 8 * VP + pos;
+  }
   bf16x8 kreg[K_PER_T];
   bf16x8 vreg[V_PER_T][4];
 
   auto load_tile = [&](int t) {
     const int kt0 = t * BN;
+    const __bf16* kb = kg + static_cast<size_t>(kt0) * rs;
+    const __bf16* vb = vg + static_cast<size_t>(kt0) * rs;
+    const int lim = L - kt0;  // rows at or past lim are outside the segment
+    if (lim >= BN) {
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int id = tid + i * NT;
-      if (K_CHUNKS % NT == 0 || id < K_CHUNKS) {
-        const int key = id / (D / 8), part = id % (D / 8);
-        const int row = kt0 + key;
-        kreg[i] = row < L ? *reinterpret_cast<const bf16x8*>(kg + row * rs + part * 8) : bf16x8{};
-      }
-    }
+      for (int i = 0; i < K_PER_T; ++i)
+        if (K_CHUNKS % NT == 0 || k_row[i] < BN) kreg[i] = *reinterpret_cast<const bf16x8*>(kb + k_goff[i]);
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (V_UNITS % NT == 0 || u < V_UNITS) {
-        const int kq = u % (BN / 4), cg = u / (BN / 4);
+      for (int i = 0; i < V_PER_T; ++i)
+        if (V_UNITS % NT == 0 || v_row[i] < BN) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int row = kt0 + 4 * kq + j;
-          vreg[i][j] = row < L ? *reinterpret_cast<const bf16x8*>(vg + row * rs + cg * 8) : bf16x8{};
+          for (int j = 0; j < 4; ++j) vreg[i][j] = *reinterpret_cast<const bf16x8*>(vb + v_goff[i] + j * rs);
         }
-      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < K_PER_T; ++i)
+        kreg[i] = k_row[i] < lim ? *reinterpret_cast<const bf16x8*>(kb + k_goff[i]) : bf16x8{};
+#pragma unroll
+      for (int i = 0; i < V_PER_T; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vreg[i][j] = v_row[i] + j < lim ? *reinterpret_cast<const bf16x8*>(vb + v_goff[i] + j * rs) : bf16x8{};
     }
   };
 
@@ -189,149 +224,120 @@ void attn_fwd_bf16(KernelArgs a) {
     __bf16* ks = lds + buf * TL::kStageElems;
     __bf16* vt = ks + TL::kKElems;
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int id = tid + i * NT;
-      if (K_CHUNKS % NT == 0 || id < K_CHUNKS) {
-        const int key = id / (D / 8), part = id % (D / 8);
-        *reinterpret_cast<bf16x8*>(ks + key * KP + part * 8) = kreg[i];
-      }
-    }
+    for (int i = 0; i < K_PER_T; ++i)
+      if (K_CHUNKS % NT == 0 || k_row[i] < BN) *reinterpret_cast<bf16x8*>(ks + k_loff[i]) = kreg[i];
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int u = tid + i * NT;
-      if (V_UNITS % NT == 0 || u < V_UNITS) {
-        const int kq = u % (BN / 4), cg = u / (BN / 4);
-        // keys 4kq..4kq+3 = 16G + 8a + 4b + [0,4) go to position 16G + 8b + 4a
-        const int pos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+    for (int i = 0; i < V_PER_T; ++i)
+      if (V_UNITS % NT == 0 || v_row[i] < BN) {
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) {
           bf16x4 col = {vreg[i][0][ch], vreg[i][1][ch], vreg[i][2][ch], vreg[i][3][ch]};
-          *reinterpret_cast<bf16x4*>(vt + (cg * 8 + ch) * VP + pos) = col;
+          *reinterpret_cast<bf16x4*>(vt + v_loff[i] + ch * VP) = col;
         }
       }
-    }
   };
 
-  // ---- running state: lane holds one query per 32-query block
-  f32x16 o[QB][CT];
+  // ---- running state of this lane's query
+  f32x16 o[CT];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) o[qb][ct] = f32x16{};
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.0f; }
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x16{};
+  float m_run = 0.0f, l_run = 0.0f;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   load_tile(0);
   store_tile(0);
   __syncthreads();
 
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-
-  // One softmax step over SB blocks of 32 keys: S^T = K Q^T, online-softmax update,
-  // O^T += V^T P^T.  MASKED is a compile-time flag so interior steps carry no
+  // One softmax step of 64 keys: S^T = K Q^T, probabilities against the reference maximum,
+  // O^T += V^T P^T.  MASKED is a compile-time flag so interior tiles carry no
   // per-score checks.
-  auto step = [&](auto masked_tag, const __bf16* ks, const __bf16* vt, int kb0, int key0, bool first) {
+  auto tile_step = [&](auto masked_tag, const __bf16* ks, const __bf16* vt, int kb0, int key0, bool first) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[QB][SB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int b = 0; b < SB; ++b) s[qb][b] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < KS; ++st)
-#pragma unroll
-      for (int b = 0; b < SB; ++b) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][st], s[qb][b], 0, 0, 0);
-      }
-
+    f32x16 s[NB];
     // keys past the segment end, and (causal) keys after the query, take no weight
-    auto dead = [&](int qb, int b, int r) {
+    auto dead = [&](int b, int r) {
       const int key = key0 + b * 32 + acc_row(r, hf);
-      return key >= L || (a.causal && key > q0 + (wave * QB + qb) * 32 + n);
+      return key >= L || (a.causal && key > qr);
     };
-    if constexpr (MASKED) {
+    auto scores = [&]() {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
-        for (int b = 0; b < SB; ++b)
+      for (int st = 0; st < KS; ++st)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
+          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[b], 0, 0, 0);
+        }
+      if constexpr (MASKED) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (dead(qb, b, r)) s[qb][b][r] = -INFINITY;
-    }
-
-    // step row max and the (lazy) running-max refresh
-    float m_blk[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
-#pragma unroll
-      for (int b = 0; b < SB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][b][r]);
-      m_blk[qb] = half_swap_max(mx);
-    }
-    if (first) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) m_run[qb] = m_blk[qb];
-    } else {
-      bool need = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) need |= (m_blk[qb] - m_run[qb]) * c > kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float m_new = fmaxf(m_run[qb], m_blk[qb]);
-          const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c);
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) o[qb][ct] *= alpha;
-        }
+            if (dead(b, r)) s[b][r] = -INFINITY;
       }
-    }
+    };
+    auto row_max = [&]() {
+      float mx = s[0][0];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+      return half_swap_max(mx);
+    };
+    scores();
+    if (first) m_run = row_max();
 
-    // probabilities -> bf16 B operands of the PV product; row sums of the same values
-    bf16x8 pk[QB][SB][2];
+    // probabilities -> bf16 B operands of the PV product; this lane's share of the
+    // row sum, over the same rounded values
+    bf16x8 pk[NB][2];
+    float lsum;
+    auto probabilities = [&]() {
+      const float mc = m_run * c;
+      lsum = 0.0f;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mc = m_run[qb] * c;
-      float lsum = 0.0f;
-#pragma unroll
-      for (int b = 0; b < SB; ++b)
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           bf16x8 pv;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][b][8 * h2 + e], c, -mc));
-            if constexpr (MASKED) p = dead(qb, b, 8 * h2 + e) ? 0.0f : p;
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e], c, -mc));
+            if constexpr (MASKED) p = dead(b, 8 * h2 + e) ? 0.0f : p;
             pv[e] = static_cast<__bf16>(p);
           }
-          pk[qb][b][h2] = pv;
+          pk[b][h2] = pv;
 #pragma unroll
           for (int e = 0; e < 8; e += 2)
             lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lsum, false);
         }
-      l_run[qb] += lsum;
+    };
+    probabilities();
+    // A stale maximum shows as a huge (or non-finite) partial sum: recompute the
+    // scores, refresh the maximum, rescale, redo.  Recomputing S here (rare) instead
+    // of keeping it live keeps the common path inside the register budget.
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit))) {
+      scores();
+      const float m_new = fmaxf(m_run, row_max());
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) scale_in_place(o[ct], alpha);
+      probabilities();
     }
+    l_run += lsum;
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int b = 0; b < SB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + (ct * 32 + n) * VP + (kb0 + b) * 32 +
-                                                             h2 * 16 + 8 * hf);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[qb][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[qb][b][h2], o[qb][ct], 0, 0, 0);
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8*>(vt + (ct * 32 + n) * VP + (kb0 + b) * 32 + h2 * 16 + 8 * hf);
+          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[b][h2], o[ct], 0, 0, 0);
         }
   };
 
@@ -342,36 +348,31 @@ void attn_fwd_bf16(KernelArgs a) {
     const __bf16* vt = ks + TL::kKElems;
 #pragma unroll
     for (int j = 0; j < NSTEP; ++j) {
-      const int key0 = t * BN + j * SB * 32;
-      if (key0 >= kend) break;  // workgroup-uniform: the tile's remaining keys are all past the end
-      const bool first = (t == 0) && (j == 0);
-      const bool masked = (key0 + SB * 32 > L) || (a.causal && key0 + SB * 32 - 1 > q0 + wave * QB * 32);
+      const int key0 = t * BN + j * TL::kStepKeys;
+      if (key0 >= kend) break;  // workgroup-uniform: the rest of the tile is past the end
+      const bool masked = (key0 + TL::kStepKeys > L) || (a.causal && key0 + TL::kStepKeys - 1 > qmin);
       if (masked)
-        step(std::true_type{}, ks, vt, j * SB, key0, first);
+        tile_step(std::true_type{}, ks, vt, j * NB, key0, t == 0 && j == 0);
       else
-        step(std::false_type{}, ks, vt, j * SB, key0, first);
+        tile_step(std::false_type{}, ks, vt, j * NB, key0, t == 0 && j == 0);
     }
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: O / l, bf16 (round to nearest even), rows inside the segment only
+  const float inv = 1.0f / half_swap_sum(l_run);
+  if (qr < L) {
+    __bf16* dst = og + static_cast<size_t>(qr) * rs + 4 * hf;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.0f / half_swap_sum(l_run[qb]);
-    const int qr = q0 + (wave * QB + qb) * 32 + n;
-    if (qr < L) {
-      __bf16* dst = og + static_cast<size_t>(qr) * rs + 4 * hf;
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 val;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          bf16x4 val;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(o[qb][ct][4 * r4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(dst + ct * 32 + r4 * 8) = val;
-        }
-    }
+        for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(o[ct][4 * r4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + ct * 32 + r4 * 8) = val;
+      }
   }
 }
 
