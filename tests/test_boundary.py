@@ -52,15 +52,15 @@ def test_supported_domain(lib):
 
 def test_lds_bytes_arithmetic(lib):
     """The LDS a workgroup asks for: two stages of a 128-key K tile (pitch d+8) and a
-    transposed V tile (d rows, pitch 136) in bf16; two stages of 32-key K and V tiles
+    row-major 128-key V tile (pitch d) in bf16; two stages of 32-key K and V tiles
     (pitch d+4) in f32.  Every supported width fits the 160 KiB of one CU."""
     for d in (64, 96, 128):
-        want_bf16 = 2 * (128 * (d + 8) + d * (128 + 8)) * 2
+        want_bf16 = 2 * (128 * (d + 8) + 128 * d) * 2
         want_f32 = 2 * 2 * 32 * (d + 4) * 4
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_BF16) == want_bf16
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_F32) == want_f32
         assert want_bf16 <= 160 * 1024 and want_f32 <= 160 * 1024
-    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 105472
+    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 102400
     assert mg.mgattn_dense_lds_bytes(80, mg.MGATTN_BF16) == -3
     assert mg.mgattn_dense_lds_bytes(96, 7) == -2
     assert mg.mgattn_dense_block_m(96, mg.MGATTN_BF16) == 256

@@ -7,35 +7,34 @@
 // same function with a running online softmax; this kernel does too, designed for
 // CDNA4 rather than after that CUDA kernel.
 //
-// Layout of the work (one workgroup = 8 waves = one (segment, head, 256-query tile);
-// two waves share each SIMD, so one wave's softmax overlaps the other's MFMAs):
-//   * Each wave owns 32 queries (one 32-query block).  Scores are computed
-//     transposed, S^T = K * Q^T, with v_mfma_f32_32x32x16_bf16: K is the A operand
-//     (keys are MFMA rows), Q^T the B operand (queries are MFMA columns).  In the
-//     32x32 accumulator a lane then holds ONE query and 16 of the 32 keys (rows
-//     8*(r/4) + 4*(lane/32) + r%4), so the row max and row sum are in-lane chains
-//     plus a single exchange between lanes l and l^32 (v_permlane32_swap).
-//   * head_dim is the contraction of S^T: D/16 MFMA k-steps (96 = 6 x 16).
-//   * O^T = V^T * P^T, again 32x32x16: V^T is the A operand, P^T the B operand.  A
-//     lane's P^T operand is exactly the 8 probabilities it already holds for one
-//     16-key group, converted to bf16 in place: no cross-lane shuffle of P.  The
-//     matching V^T operand is read from LDS, where V is stored transposed and with
-//     the keys of each 16-key group permuted ([0-3, 8-11 | 4-7, 12-15]) so that
-//     those 8 keys are one contiguous 16-byte read.  O^T is D/32 accumulators of
-//     32x32 (96 = 3 x 32); a lane holds one query's 16 output channels per tile.
-//   * K/V tiles of 128 keys go HBM -> registers -> LDS, double-buffered: the next
-//     tile's global loads are in flight during the current tile's MFMA work, and
-//     one barrier per tile separates the buffers.  LDS rows are padded (K pitch
-//     D+8, V^T pitch 128+8 elements) so every 16-byte MFMA operand read is free of
-//     bank conflicts.  A tile is two softmax steps of 64 keys (32 scores per lane).
-//   * Softmax uses exp2 with scale*log2(e) folded into one FMA per score, against a
-//     reference maximum per query: the first tile's row maximum.  Later tiles do not
-//     recompute the maximum.  Exactness does not depend on the reference (numerator
-//     and denominator share it); only range does, so a tile whose partial row sum
-//     exceeds 2^64 (or is not finite) is redone after refreshing the reference to
-//     the true maximum and rescaling O and the row sum (a rare, wave-uniform path).
-//   * The row sum adds the bf16-rounded probabilities that feed the PV product
-//     (v_dot2 with ones), so the weights stay normalised.
+// One workgroup = 8 waves = one (segment, head, 256-query tile).
+//   * Each wave owns 32 queries.  Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16: K is the A operand (keys are MFMA rows), Q^T the B
+//     operand (queries are MFMA columns).  In the 32x32 accumulator a lane then holds
+//     ONE query and 16 of the 32 keys (rows 8*(r/4) + 4*(lane/32) + r%4), so the row
+//     max and row sum are in-lane chains plus one exchange between lanes l and l^32
+//     (v_permlane32_swap).  head_dim is the contraction: D/16 MFMA steps (96 = 6x16).
+//   * O^T = V^T P^T, again 32x32x16: P^T is the B operand and is exactly the 8
+//     probabilities a lane already holds for one 16-key group, converted to bf16 in
+//     place (no cross-lane shuffle).  The V^T A operand is read from a row-major V
+//     tile with two ds_read_b64_tr_b16 (the LDS transpose read: within 16 lanes,
+//     lane i gets element i%4 of the 8 bytes addressed by lanes 4j + i/4, j = 0..3),
+//     addressed so each lane receives 4 keys of its own channel.  O^T is D/32
+//     accumulators of 32x32 (96 = 3 x 32).
+//   * K/V tiles of 128 keys go HBM -> LDS by LDS DMA (global_load_lds_dwordx4: each
+//     lane's 16 bytes land at M0 + 16*lane, no registers involved), double-buffered.
+//     K rows are padded to 13 x 16 bytes (pitch 208 B: every 16-byte MFMA operand
+//     read is free of bank conflicts); the padding slots are masked-off lanes.
+//   * Softmax (per 64-key step) uses exp2 with scale*log2(e) folded into one FMA per
+//     score.  The running maximum is refreshed only when a step's maximum exceeds it
+//     by more than 2^8 in probability terms (decided per wave), so the O rescale is
+//     skipped on almost every step; exact, because numerator and denominator share
+//     the reference.  The row sum adds the bf16-rounded probabilities that feed the
+//     PV product (v_dot2 with ones), so the weights stay normalised.
+//   * Ping-pong: waves 0-3 and 4-7 share SIMDs pairwise and run the same sequence of
+//     MFMA phases (PV of the previous step + QK of the next, 24 MFMAs) and VALU phases
+//     (softmax) one phase apart, with a workgroup barrier closing every phase; so
+//     each SIMD always has one wave feeding the matrix core and one on the VALU.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,8 +59,8 @@ struct KernelArgs {
   void* o;
   int32_t H;
   int32_t causal;
-  float c;        // |scale| * log2(e)
-  int32_t negate; // 1 when scale < 0 (Q is negated in registers; exact)
+  float c;        // |scale| * log2(e), or 1 when scale == 0 (always > 0)
+  int32_t qsign;  // sign of scale: Q is multiplied by +1, -1 or 0 in registers (exact)
   SegTable table;
 };
 
@@ -73,15 +72,21 @@ struct Bf16Tile {
   static constexpr int kBlockN = 128;                    // keys per LDS tile
   static constexpr int kStepKeys = 64;                   // keys per softmax step
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kKPitch = D + 8;                  // K row pitch (elements)
-  static constexpr int kVPitch = kBlockN + 8;            // V^T row pitch (elements)
+  static constexpr int kKSlots = D / 8 + 1;              // 16-byte slots per K row (+1 pad)
+  static constexpr int kKPitch = kKSlots * 8;            // K row pitch (elements)
+  static constexpr int kVPitch = D;                      // V row pitch (elements)
   static constexpr int kKElems = kBlockN * kKPitch;
-  static constexpr int kVElems = D * kVPitch;
+  static constexpr int kVElems = kBlockN * kVPitch;
   static constexpr int kStageElems = kKElems + kVElems;
   static constexpr int kStages = 2;
   static constexpr int kLdsBytes = kStages * kStageElems * 2;
+  // LDS DMA instructions (64 lanes x 16 bytes) per tile
+  static constexpr int kKDma = (kBlockN * kKSlots + 63) / 64;
+  static constexpr int kVDma = kBlockN * D / 8 / 64;
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head_dim must be a multiple of 32 up to 128");
   static_assert(kBlockN % kStepKeys == 0 && kStepKeys % 32 == 0, "LDS tile must hold whole softmax steps");
+  static_assert((kBlockN * D / 8) % 64 == 0, "V tile must be whole DMA instructions");
+  static_assert(kKElems % 8 == 0 && kStageElems % 8 == 0, "LDS regions must stay 16-byte aligned");
 };
 
 // Exchange with lane l^32 and combine (max or sum) -- one v_permlane32_swap.
@@ -97,16 +102,27 @@ __device__ inline float half_swap_sum(float x) {
 // Key (relative to the 32-key block) held in accumulator register r by lane half hf.
 __device__ constexpr int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
-// In-place v *= a on every element.  The tied register operand keeps the scaled
-// accumulator in the registers it already occupies, so the (rare) rescale branch
-// does not force the compiler to copy the accumulators at the branch join.
-__device__ inline void scale_in_place(f32x16& v, float a) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float t = v[i];
-    asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t) : "v"(a));
-    v[i] = t;
-  }
+typedef __bf16 bf16x4_raw __attribute__((__vector_size__(4 * sizeof(__bf16))));
+#define MGATTN_LDS __attribute__((address_space(3)))
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((MGATTN_LDS const void*)p));
+}
+
+// LDS DMA of 16 bytes per active lane: lane l's bytes at g land at LDS address
+// m0 + 16*l.  Written as asm (no output registers; the address is read at issue) so
+// that the compiler does not order later LDS reads behind it: the one wait for the
+// DMA is the explicit vmcnt(0) before the barrier that publishes the tile.
+__device__ inline void dma16(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory");
+}
+__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// LDS transpose read: 4 bf16 (see the layout note at the top of this file).
+__device__ inline bf16x4 ds_read_tr(const __bf16* p) {
+  const bf16x4_raw r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MGATTN_LDS bf16x4_raw*)p);
+  return __builtin_bit_cast(bf16x4, r);
 }
 
 template <int D>
@@ -114,19 +130,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_pe
 void attn_fwd_bf16(KernelArgs a) {
   using TL = Bf16Tile<D>;
   constexpr int BM = TL::kBlockM, BN = TL::kBlockN;
-  constexpr int KS = D / 16;   // MFMA k-steps over head_dim
-  constexpr int CT = D / 32;   // 32-channel output tiles
-  constexpr int NB = TL::kStepKeys / 32;  // 32-key blocks per softmax step
-  constexpr int NSTEP = BN / TL::kStepKeys;  // softmax steps per LDS tile
-  constexpr int KP = TL::kKPitch, VP = TL::kVPitch;
-  constexpr int NT = TL::kThreads;
-  constexpr int K_CHUNKS = BN * D / 8;         // 16-byte pieces of a K tile
-  constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-  constexpr int V_UNITS = (BN / 4) * (D / 8);  // 4 keys x 8 channels each
-  constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
-  // A row's partial sum over one tile above 2^64 means the reference maximum is stale
-  // by a wide margin: the tile is redone against a refreshed maximum.
-  constexpr float kSumLimit = 18446744073709551616.0f;
+  constexpr int SK = TL::kStepKeys;  // keys per softmax step
+  constexpr int NB = SK / 32;        // 32-key blocks per softmax step
+  constexpr int NSTEP = BN / SK;     // softmax steps per LDS tile
+  constexpr int KS = D / 16;         // MFMA k-steps over head_dim
+  constexpr int CT = D / 32;         // 32-channel output tiles
+  constexpr int KP = TL::kKPitch, VP = TL::kVPitch, KSL = TL::kKSlots;
+  constexpr int KDMA = TL::kKDma, VDMA = TL::kVDma;
+  constexpr int KDMA_W = (KDMA + TL::kWaves - 1) / TL::kWaves;  // per wave (upper bound)
+  constexpr int VDMA_W = (VDMA + TL::kWaves - 1) / TL::kWaves;
+  constexpr float kRescaleLog2 = 8.0f;  // refresh the running max past 2^8 growth
   static_assert(TL::kQBlocks == 1, "one 32-query block per wave");
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
@@ -143,7 +156,8 @@ void attn_fwd_bf16(KernelArgs a) {
   __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + base;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index, marked wave-uniform so branches on it are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31;
   const int hf = lane >> 5;
@@ -161,80 +175,59 @@ void attn_fwd_bf16(KernelArgs a) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
   }
-  if (a.negate) {
+  if (a.qsign != 1) {
+    const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = -qf[s];
+    for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
   }
 
   const int kend = a.causal ? min(L, q0 + BM) : L;
   const int ntiles = (kend + BN - 1) / BN;
+  const int nsteps = (kend + SK - 1) / SK;
 
-  // ---- tile staging: per-thread offsets are fixed, a tile only moves the base
-  int k_row[K_PER_T], k_goff[K_PER_T], k_loff[K_PER_T];
+  // ---- LDS DMA plan.  DMA instruction i of a tile fills 64 consecutive 16-byte
+  // slots (1 KB); wave w issues instructions w, w+8, ...  K slot s is row s/KSL,
+  // piece s%KSL (piece D/8 is padding: lane masked off).  V slot s is row s/(D/8),
+  // piece s%(D/8).  Rows past the segment end are clamped to its last row: their
+  // keys are masked (p = 0) and the clamped data is finite.
+  int k_row[KDMA_W], k_off[KDMA_W];
 #pragma unroll
-  for (int i = 0; i < K_PER_T; ++i) {
-    const int id = tid + i * NT;
-    const int key = id / (D / 8), part = id % (D / 8);
-    k_row[i] = (K_CHUNKS % NT == 0 || id < K_CHUNKS) ? key : BN;  // BN: never loaded
-    k_goff[i] = key * rs + part * 8;
-    k_loff[i] = key * KP + part * 8;
+  for (int u = 0; u < KDMA_W; ++u) {
+    const int slot = (wave + TL::kWaves * u) * 64 + lane;
+    const int row = slot / KSL, piece = slot % KSL;
+    k_row[u] = (piece < D / 8 && row < BN) ? row : -1;  // -1: lane idle
+    k_off[u] = piece * 8;
   }
-  int v_row[V_PER_T], v_goff[V_PER_T], v_loff[V_PER_T];
+  int v_row[VDMA_W], v_off[VDMA_W];
 #pragma unroll
-  for (int i = 0; i < V_PER_T; ++i) {
-    const int u = tid + i * NT;
-    const int kq = u % (BN / 4), cg = u / (BN / 4);
-    // keys 4kq..4kq+3 = 16G + 8a + 4b + [0,4) go to position 16G + 8b + 4a of each V^T row
-    const int pos = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
-    v_row[i] = (V_UNITS % NT == 0 || u < V_UNITS) ? 4 * kq : BN;
-    v_goff[i] = 4 * kq * rs + cg * 8;
-    v_loff[i] = cg * 8 * VP + pos;
+  for (int u = 0; u < VDMA_W; ++u) {
+    const int slot = (wave + TL::kWaves * u) * 64 + lane;
+    v_row[u] = slot / (D / 8);
+    v_off[u] = (slot % (D / 8)) * 8;
   }
-  bf16x8 kreg[K_PER_T];
-  bf16x8 vreg[V_PER_T][4];
-
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t) {
     const int kt0 = t * BN;
+    const int last = L - 1 - kt0;  // last valid row of this tile (>= 0)
     const __bf16* kb = kg + static_cast<size_t>(kt0) * rs;
     const __bf16* vb = vg + static_cast<size_t>(kt0) * rs;
-    const int lim = L - kt0;  // rows at or past lim are outside the segment
-    if (lim >= BN) {
+    __bf16* kl = lds + (t & 1) * TL::kStageElems;
+    __bf16* vl = kl + TL::kKElems;
 #pragma unroll
-      for (int i = 0; i < K_PER_T; ++i)
-        if (K_CHUNKS % NT == 0 || k_row[i] < BN) kreg[i] = *reinterpret_cast<const bf16x8*>(kb + k_goff[i]);
-#pragma unroll
-      for (int i = 0; i < V_PER_T; ++i)
-        if (V_UNITS % NT == 0 || v_row[i] < BN) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) vreg[i][j] = *reinterpret_cast<const bf16x8*>(vb + v_goff[i] + j * rs);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < K_PER_T; ++i)
-        kreg[i] = k_row[i] < lim ? *reinterpret_cast<const bf16x8*>(kb + k_goff[i]) : bf16x8{};
-#pragma unroll
-      for (int i = 0; i < V_PER_T; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vreg[i][j] = v_row[i] + j < lim ? *reinterpret_cast<const bf16x8*>(vb + v_goff[i] + j * rs) : bf16x8{};
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-    __bf16* ks = lds + buf * TL::kStageElems;
-    __bf16* vt = ks + TL::kKElems;
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i)
-      if (K_CHUNKS % NT == 0 || k_row[i] < BN) *reinterpret_cast<bf16x8*>(ks + k_loff[i]) = kreg[i];
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i)
-      if (V_UNITS % NT == 0 || v_row[i] < BN) {
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          bf16x4 col = {vreg[i][0][ch], vreg[i][1][ch], vreg[i][2][ch], vreg[i][3][ch]};
-          *reinterpret_cast<bf16x4*>(vt + v_loff[i] + ch * VP) = col;
-        }
+    for (int u = 0; u < KDMA_W; ++u) {
+      const int i = wave + TL::kWaves * u;
+      if (KDMA % TL::kWaves == 0 || i < KDMA) {
+        if (k_row[u] >= 0)
+          dma16(kb + static_cast<size_t>(min(k_row[u], last)) * rs + k_off[u],
+                __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
       }
+    }
+#pragma unroll
+    for (int u = 0; u < VDMA_W; ++u) {
+      const int i = wave + TL::kWaves * u;
+      if (VDMA % TL::kWaves == 0 || i < VDMA)
+        dma16(vb + static_cast<size_t>(min(v_row[u], last)) * rs + v_off[u],
+              __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
+    }
   };
 
   // ---- running state of this lane's query
@@ -243,120 +236,173 @@ void attn_fwd_bf16(KernelArgs a) {
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x16{};
   float m_run = 0.0f, l_run = 0.0f;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  f32x16 s[NB];      // scores of the current step (written by an MFMA phase)
+  bf16x8 pk[NB][2];  // probabilities of the current step (written by a VALU phase)
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // Where step j's keys live: LDS buffer of its tile, and its first 32-key block.
+  auto step_buf = [&](int j) { return lds + ((j / NSTEP) & 1) * TL::kStageElems; };
+  auto step_b = [&](int j) { return (j % NSTEP) * NB; };
 
-  // One softmax step of 64 keys: S^T = K Q^T, probabilities against the reference maximum,
-  // O^T += V^T P^T.  MASKED is a compile-time flag so interior tiles carry no
-  // per-score checks.
-  auto tile_step = [&](auto masked_tag, const __bf16* ks, const __bf16* vt, int kb0, int key0, bool first) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 s[NB];
-    // keys past the segment end, and (causal) keys after the query, take no weight
-    auto dead = [&](int b, int r) {
-      const int key = key0 + b * 32 + acc_row(r, hf);
-      return key >= L || (a.causal && key > qr);
-    };
-    auto scores = [&]() {
+  // V^T transpose-read lane addressing: lane r of each 16-lane group reads row
+  // (key) r/4 (+4 for the upper lane half, +8 for the second read) at channel
+  // 16*(group%2) + 4*(r%4) of the 32-channel tile.
+  const int tr_row = ((lane & 15) >> 2) + 4 * hf;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // MFMA work: O^T += V^T P^T for step j, and S^T = K Q^T for step j (12 MFMAs each).
+  auto mfma_pv = [&](int j) {
+    const __bf16* vt = step_buf(j) + TL::kKElems;
+    const int kb0 = step_b(j);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int st = 0; st < KS; ++st)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const __bf16* vrow = vt + ((kb0 + b) * 32 + h2 * 16 + tr_row) * VP + tr_col;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
-          s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[b], 0, 0, 0);
+        for (int ct = 0; ct < CT; ++ct) {
+          const bf16x4 lo = ds_read_tr(vrow + ct * 32);
+          const bf16x4 hi = ds_read_tr(vrow + 8 * VP + ct * 32);
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[b][h2], o[ct], 0, 0, 0);
         }
-      if constexpr (MASKED) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (dead(b, r)) s[b][r] = -INFINITY;
       }
-    };
-    auto row_max = [&]() {
-      float mx = s[0][0];
+  };
+  auto mfma_qk = [&](int j) {
+    const __bf16* ks = step_buf(j);
+    const int kb0 = step_b(j);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-      return half_swap_max(mx);
-    };
-    scores();
-    if (first) m_run = row_max();
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[b], 0, 0, 0);
+      }
+  };
 
-    // probabilities -> bf16 B operands of the PV product; this lane's share of the
-    // row sum, over the same rounded values
-    bf16x8 pk[NB][2];
-    float lsum;
-    auto probabilities = [&]() {
-      const float mc = m_run * c;
-      lsum = 0.0f;
+  // VALU phase j: online softmax of step j's scores into bf16 probabilities.  Keys
+  // past the segment end and (causal) keys after the query get s = -inf, hence p = 0
+  // (c is always positive).
+  auto valu_phase = [&](int j) {
+    const int key0 = j * SK;
+    if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          bf16x8 pv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e], c, -mc));
-            if constexpr (MASKED) p = dead(b, 8 * h2 + e) ? 0.0f : p;
-            pv[e] = static_cast<__bf16>(p);
-          }
-          pk[b][h2] = pv;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lsum, false);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + b * 32 + acc_row(r, hf);
+          if (key >= L || (a.causal && key > qr)) s[b][r] = -INFINITY;
         }
-    };
-    probabilities();
-    // A stale maximum shows as a huge (or non-finite) partial sum: recompute the
-    // scores, refresh the maximum, rescale, redo.  Recomputing S here (rare) instead
-    // of keeping it live keeps the common path inside the register budget.
-    if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumLimit))) {
-      scores();
-      const float m_new = fmaxf(m_run, row_max());
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+    const float m_blk = half_swap_max(mx);
+    if (j == 0) {
+      m_run = m_blk;
+    } else if (__builtin_amdgcn_ballot_w64((m_blk - m_run) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_blk);
       const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) scale_in_place(o[ct], alpha);
-      probabilities();
+      for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
     }
-    l_run += lsum;
-
-    // O^T += V^T P^T
+    const float mc = m_run * c;
+    float lsum = 0.0f;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 pv;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const bf16x8 vf =
-              *reinterpret_cast<const bf16x8*>(vt + (ct * 32 + n) * VP + (kb0 + b) * 32 + h2 * 16 + 8 * hf);
-          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[b][h2], o[ct], 0, 0, 0);
-        }
+        for (int e = 0; e < 8; ++e)
+          pv[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e], c, -mc)));
+        pk[b][h2] = pv;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[e], pv[e + 1]}, ones, lsum, false);
+      }
+    l_run += lsum;
   };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    const __bf16* ks = lds + buf * TL::kStageElems;
-    const __bf16* vt = ks + TL::kKElems;
-#pragma unroll
-    for (int j = 0; j < NSTEP; ++j) {
-      const int key0 = t * BN + j * TL::kStepKeys;
-      if (key0 >= kend) break;  // workgroup-uniform: the rest of the tile is past the end
-      const bool masked = (key0 + TL::kStepKeys > L) || (a.causal && key0 + TL::kStepKeys - 1 > qmin);
-      if (masked)
-        tile_step(std::true_type{}, ks, vt, j * NB, key0, t == 0 && j == 0);
-      else
-        tile_step(std::false_type{}, ks, vt, j * NB, key0, t == 0 && j == 0);
+  // Tile staging by phase: tile k+1's DMA is issued at the start of phase 4k+2, after
+  // the last read of the buffer it replaces (phase 4k+1), and waited for at the end
+  // of phase 4k+3, before the barrier that publishes it for phase 4k+4.
+  auto stage_begin = [&](int p) {
+    if ((p & 3) == 2 && (p >> 2) + 1 < ntiles) issue_tile((p >> 2) + 1);
+  };
+  auto stage_end = [&](int p) {
+    if ((p & 3) == 3 && (p >> 2) + 1 < ntiles) dma_wait();
+  };
+
+  issue_tile(0);
+  dma_wait();
+  __syncthreads();
+
+  // Phase schedule.  A wave's own sequence is MFMA(0), VALU(0), MFMA(1), VALU(1), ...,
+  // VALU(n-1), MFMA(n): MFMA(j) is the PV product of step j-1 and the QK product of
+  // step j.  Waves 0-3 run slot i in phase i; waves 4-7 (which share the SIMDs of
+  // waves 0-3) run it in phase i+1.  In every phase one wave of each SIMD issues
+  // MFMAs while the other runs its softmax, and a barrier closes each phase; both
+  // groups pass the same 2n+2 barriers.
+  const int n_st = nsteps;
+  if (wave < 4) {
+    stage_begin(0);
+    mfma_qk(0);
+    stage_end(0);
+    __syncthreads();
+    for (int j = 0; j + 1 < n_st; ++j) {
+      stage_begin(2 * j + 1);
+      valu_phase(j);
+      stage_end(2 * j + 1);
+      __syncthreads();
+      stage_begin(2 * j + 2);
+      mfma_pv(j);
+      mfma_qk(j + 1);
+      stage_end(2 * j + 2);
+      __syncthreads();
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    stage_begin(2 * n_st - 1);
+    valu_phase(n_st - 1);
+    stage_end(2 * n_st - 1);
+    __syncthreads();
+    stage_begin(2 * n_st);
+    mfma_pv(n_st - 1);
+    stage_end(2 * n_st);
+    __syncthreads();
+    stage_begin(2 * n_st + 1);
+    stage_end(2 * n_st + 1);
+    __syncthreads();
+  } else {
+    stage_begin(0);
+    stage_end(0);
+    __syncthreads();
+    stage_begin(1);
+    mfma_qk(0);
+    stage_end(1);
+    __syncthreads();
+    for (int j = 0; j + 1 < n_st; ++j) {
+      stage_begin(2 * j + 2);
+      valu_phase(j);
+      stage_end(2 * j + 2);
+      __syncthreads();
+      stage_begin(2 * j + 3);
+      mfma_pv(j);
+      mfma_qk(j + 1);
+      stage_end(2 * j + 3);
+      __syncthreads();
+    }
+    stage_begin(2 * n_st);
+    valu_phase(n_st - 1);
+    stage_end(2 * n_st);
+    __syncthreads();
+    stage_begin(2 * n_st + 1);
+    mfma_pv(n_st - 1);
+    stage_end(2 * n_st + 1);
     __syncthreads();
   }
 

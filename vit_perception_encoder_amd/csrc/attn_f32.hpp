@@ -75,7 +75,7 @@ void attn_fwd_f32(KernelArgs a) {
     for (int j = 0; j < HD / 4; ++j) {
       const f32x4 x = p[j];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf[4 * j + e] = a.negate ? -x[e] : x[e];
+      for (int e = 0; e < 4; ++e) qf[4 * j + e] = x[e] * static_cast<float>(a.qsign);
     }
   } else {
 #pragma unroll

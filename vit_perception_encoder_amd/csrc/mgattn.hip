@@ -137,8 +137,11 @@ int mgattn_dense(const void* q, const void* k, const void* v, void* out, const i
   args.o = out;
   args.H = H;
   args.causal = causal;
-  args.c = static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);  // log2(e)
-  args.negate = scale < 0.0f ? 1 : 0;
+  // c = |scale| * log2(e) multiplies the scores inside exp2; the sign of scale goes
+  // into Q (exact).  For scale == 0 the scores vanish (Q * 0) and c = 1 keeps masked
+  // keys at exp2(-inf) = 0.
+  args.c = scale == 0.0f ? 1.0f : static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);
+  args.qsign = scale > 0.0f ? 1 : (scale < 0.0f ? -1 : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == MGATTN_BF16) {
     switch (d) {
