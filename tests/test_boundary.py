@@ -51,16 +51,20 @@ def test_supported_domain(lib):
 
 
 def test_lds_bytes_arithmetic(lib):
-    """The LDS a workgroup asks for: two stages of a 128-key K tile (pitch d+8) and a
-    row-major 128-key V tile (pitch d) in bf16; two stages of 32-key K and V tiles
-    (pitch d+4) in f32.  Every supported width fits the 160 KiB of one CU."""
+    """The LDS a workgroup asks for.  bf16: S stages of a 128-key K tile (pitch d+8)
+    and a row-major 128-key V tile (pitch d), S = 3 when three stages fit the 160 KiB
+    of one CU, else 2.  f32: two stages of 32-key K and V tiles (pitch d+4).  The
+    bound is inclusive: d=96 bf16 asks for 153,600 bytes, inside 163,840."""
     for d in (64, 96, 128):
-        want_bf16 = 2 * (128 * (d + 8) + 128 * d) * 2
+        stage = (128 * (d + 8) + 128 * d) * 2
+        stages = 3 if 3 * stage <= 160 * 1024 else 2
+        want_bf16 = stages * stage
         want_f32 = 2 * 2 * 32 * (d + 4) * 4
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_BF16) == want_bf16
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_F32) == want_f32
         assert want_bf16 <= 160 * 1024 and want_f32 <= 160 * 1024
-    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 102400
+    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 153600
+    assert mg.mgattn_dense_lds_bytes(128, mg.MGATTN_BF16) == 135168
     assert mg.mgattn_dense_lds_bytes(80, mg.MGATTN_BF16) == -3
     assert mg.mgattn_dense_lds_bytes(96, 7) == -2
     assert mg.mgattn_dense_block_m(96, mg.MGATTN_BF16) == 256

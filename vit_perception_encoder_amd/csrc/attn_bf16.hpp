@@ -22,7 +22,10 @@
 //     addressed so each lane receives 4 keys of its own channel.  O^T is D/32
 //     accumulators of 32x32 (96 = 3 x 32).
 //   * K/V tiles of 128 keys go HBM -> LDS by LDS DMA (global_load_lds_dwordx4: each
-//     lane's 16 bytes land at M0 + 16*lane, no registers involved), double-buffered.
+//     lane's 16 bytes land at M0 + 16*lane, no registers involved) into three LDS
+//     stages (two for head_dim 128), issued two phases before they are published.
+//     The K operands of the next QK product are read from LDS during the softmax
+//     phase, so the MFMA phase issues its QK MFMAs back to back.
 //     K rows are padded to 13 x 16 bytes (pitch 208 B: every 16-byte MFMA operand
 //     read is free of bank conflicts); the padding slots are masked-off lanes.
 //   * Softmax (per 64-key step) uses exp2 with scale*log2(e) folded into one FMA per
@@ -78,7 +81,9 @@ struct Bf16Tile {
   static constexpr int kKElems = kBlockN * kKPitch;
   static constexpr int kVElems = kBlockN * kVPitch;
   static constexpr int kStageElems = kKElems + kVElems;
-  static constexpr int kStages = 2;
+  // LDS stages: three when they fit in the 160 KB of a CU (head_dim <= 96), so a tile
+  // is published a full step before its first read; two otherwise.
+  static constexpr int kStages = (3 * kStageElems * 2 <= 160 * 1024) ? 3 : 2;
   static constexpr int kLdsBytes = kStages * kStageElems * 2;
   // LDS DMA instructions (64 lanes x 16 bytes) per tile
   static constexpr int kKDma = (kBlockN * kKSlots + 63) / 64;
@@ -210,7 +215,7 @@ void attn_fwd_bf16(KernelArgs a) {
     const int last = L - 1 - kt0;  // last valid row of this tile (>= 0)
     const __bf16* kb = kg + static_cast<size_t>(kt0) * rs;
     const __bf16* vb = vg + static_cast<size_t>(kt0) * rs;
-    __bf16* kl = lds + (t & 1) * TL::kStageElems;
+    __bf16* kl = lds + (t % TL::kStages) * TL::kStageElems;
     __bf16* vl = kl + TL::kKElems;
 #pragma unroll
     for (int u = 0; u < KDMA_W; ++u) {
@@ -236,11 +241,12 @@ void attn_fwd_bf16(KernelArgs a) {
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x16{};
   float m_run = 0.0f, l_run = 0.0f;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  f32x16 s[NB];      // scores of the current step (written by an MFMA phase)
-  bf16x8 pk[NB][2];  // probabilities of the current step (written by a VALU phase)
+  f32x16 s[NB];          // scores of the current step (written by an MFMA phase)
+  bf16x8 pk[NB][2];      // probabilities of the current step (written by a VALU phase)
+  bf16x8 kpre[KS][NB];   // K operands of the next QK product (read during a VALU phase)
 
   // Where step j's keys live: LDS buffer of its tile, and its first 32-key block.
-  auto step_buf = [&](int j) { return lds + ((j / NSTEP) & 1) * TL::kStageElems; };
+  auto step_buf = [&](int j) { return lds + ((j / NSTEP) % TL::kStages) * TL::kStageElems; };
   auto step_b = [&](int j) { return (j % NSTEP) * NB; };
 
   // V^T transpose-read lane addressing: lane r of each 16-lane group reads row
@@ -267,24 +273,31 @@ void attn_fwd_bf16(KernelArgs a) {
         }
       }
   };
-  auto mfma_qk = [&](int j) {
+  auto read_k = [&](int j) {
     const __bf16* ks = step_buf(j);
     const int kb0 = step_b(j);
+#pragma unroll
+    for (int st = 0; st < KS; ++st)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        kpre[st][b] = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
+  };
+  auto mfma_qk = [&]() {
+    __builtin_amdgcn_s_setprio(1);  // MFMA phase: ahead of the other wave's softmax at issue
 #pragma unroll
     for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
     for (int st = 0; st < KS; ++st)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
-        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], s[b], 0, 0, 0);
-      }
+      for (int b = 0; b < NB; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpre[st][b], qf[st], s[b], 0, 0, 0);
   };
 
   // VALU phase j: online softmax of step j's scores into bf16 probabilities.  Keys
   // past the segment end and (causal) keys after the query get s = -inf, hence p = 0
   // (c is always positive).
   auto valu_phase = [&](int j) {
+    __builtin_amdgcn_s_setprio(0);
+    if (j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
     const int key0 = j * SK;
     if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
 #pragma unroll
@@ -329,19 +342,28 @@ void attn_fwd_bf16(KernelArgs a) {
     l_run += lsum;
   };
 
-  // Tile staging by phase: tile k+1's DMA is issued at the start of phase 4k+2, after
-  // the last read of the buffer it replaces (phase 4k+1), and waited for at the end
-  // of phase 4k+3, before the barrier that publishes it for phase 4k+4.
-  auto stage_begin = [&](int p) {
-    if ((p & 3) == 2 && (p >> 2) + 1 < ntiles) issue_tile((p >> 2) + 1);
-  };
-  auto stage_end = [&](int p) {
-    if ((p & 3) == 3 && (p >> 2) + 1 < ntiles) dma_wait();
-  };
-
-  issue_tile(0);
+  // Tile staging by phase.  Step j's K is read in VALU phase j-1 and its V in MFMA
+  // phase j+1, so tile t (steps tN .. tN+N-1) is read in phases 2tN-1 .. 2tN+2N+1 of
+  // the leading group (one later for the trailing one).  Its DMA is waited for at the
+  // end of phase W(t) = 2tN-2 (published for 2tN-1) and issued at the start of phase
+  // I(t) = max(2tN-4, 2N(t-S+1)+2): two phases of latency when the buffer it replaces
+  // (tile t-S, last read in phase 2N(t-S+1)+1) is already free.
+  constexpr int N2 = 2 * NSTEP;
+  auto issue_phase = [&](int t) { return max(N2 * t - 4, N2 * (t - TL::kStages + 1) + 2); };
+  int t_issue = 0, t_wait = 0;
+  while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++);
+  while (t_wait < ntiles && N2 * t_wait - 2 < 0) ++t_wait;
   dma_wait();
   __syncthreads();
+  auto stage_begin = [&](int p) {
+    if (t_issue < ntiles && issue_phase(t_issue) == p) issue_tile(t_issue++);
+  };
+  auto stage_end = [&](int p) {
+    if (t_wait < ntiles && N2 * t_wait - 2 == p) {
+      dma_wait();
+      ++t_wait;
+    }
+  };
 
   // Phase schedule.  A wave's own sequence is MFMA(0), VALU(0), MFMA(1), VALU(1), ...,
   // VALU(n-1), MFMA(n): MFMA(j) is the PV product of step j-1 and the QK product of
@@ -352,7 +374,8 @@ void attn_fwd_bf16(KernelArgs a) {
   const int n_st = nsteps;
   if (wave < 4) {
     stage_begin(0);
-    mfma_qk(0);
+    read_k(0);
+    mfma_qk();
     stage_end(0);
     __syncthreads();
     for (int j = 0; j + 1 < n_st; ++j) {
@@ -361,8 +384,8 @@ void attn_fwd_bf16(KernelArgs a) {
       stage_end(2 * j + 1);
       __syncthreads();
       stage_begin(2 * j + 2);
+      mfma_qk();
       mfma_pv(j);
-      mfma_qk(j + 1);
       stage_end(2 * j + 2);
       __syncthreads();
     }
@@ -382,7 +405,8 @@ void attn_fwd_bf16(KernelArgs a) {
     stage_end(0);
     __syncthreads();
     stage_begin(1);
-    mfma_qk(0);
+    read_k(0);
+    mfma_qk();
     stage_end(1);
     __syncthreads();
     for (int j = 0; j + 1 < n_st; ++j) {
@@ -391,8 +415,8 @@ void attn_fwd_bf16(KernelArgs a) {
       stage_end(2 * j + 2);
       __syncthreads();
       stage_begin(2 * j + 3);
+      mfma_qk();
       mfma_pv(j);
-      mfma_qk(j + 1);
       stage_end(2 * j + 3);
       __syncthreads();
     }
