@@ -283,7 +283,6 @@ void attn_fwd_bf16(KernelArgs a) {
         kpre[st][b] = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
   };
   auto mfma_qk = [&]() {
-    __builtin_amdgcn_s_setprio(1);  // MFMA phase: ahead of the other wave's softmax at issue
 #pragma unroll
     for (int b = 0; b < NB; ++b) s[b] = f32x16{};
 #pragma unroll
@@ -296,7 +295,6 @@ void attn_fwd_bf16(KernelArgs a) {
   // past the segment end and (causal) keys after the query get s = -inf, hence p = 0
   // (c is always positive).
   auto valu_phase = [&](int j) {
-    __builtin_amdgcn_s_setprio(0);
     if (j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
     const int key0 = j * SK;
     if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
