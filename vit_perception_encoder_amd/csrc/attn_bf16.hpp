@@ -428,19 +428,39 @@ void attn_fwd_bf16(KernelArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: O / l, bf16 (round to nearest even), rows inside the segment only
+  // ---- epilogue: O / l -> bf16 (round to nearest even), rows inside the segment
+  // only.  The wave's 32 x D tile is staged through its own LDS rows (every wave has
+  // passed the last barrier, so the K/V stages are dead) and stored as whole rows,
+  // 16 bytes per lane: in the accumulator layout a lane holds one query and 4
+  // channels per register group, which would scatter 8-byte pieces over 32 rows.
   const float inv = 1.0f / half_swap_sum(l_run);
-  if (qr < L) {
-    __bf16* dst = og + static_cast<size_t>(qr) * rs + 4 * hf;
+  constexpr int OP = D + 8;  // O row pitch in LDS (elements), rows 16-byte aligned
+  static_assert(TL::kWaves * 32 * OP <= TL::kStages * TL::kStageElems, "O staging must fit in the K/V stages");
+  __bf16* ow = lds + wave * 32 * OP;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+  for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        bf16x4 val;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(o[ct][4 * r4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + ct * 32 + r4 * 8) = val;
-      }
+      for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(o[ct][4 * r4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(ow + n * OP + ct * 32 + r4 * 8 + 4 * hf) = val;
+    }
+  constexpr int CH = D / 8;  // 16-byte pieces per row
+  constexpr int NU = 32 * CH / 64;
+  static_assert(32 * CH % 64 == 0, "whole store instructions per wave");
+  bf16x8 piece_val[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int cidx = u * 64 + lane;
+    piece_val[u] = *reinterpret_cast<const bf16x8*>(ow + (cidx / CH) * OP + (cidx % CH) * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int cidx = u * 64 + lane;
+    const int row = cidx / CH;
+    if (qmin + row < L)
+      *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(qmin + row) * rs + (cidx % CH) * 8) = piece_val[u];
   }
 }
 
