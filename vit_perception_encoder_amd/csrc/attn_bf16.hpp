@@ -170,22 +170,7 @@ void attn_fwd_bf16(KernelArgs a) {
   const int qr = q0 + wave * 32 + n;  // this lane's query (relative to the segment)
   const int qmin = q0 + wave * 32;    // the wave's first query
 
-  // ---- Q fragments (B operand of S^T): lane holds query qr, channels 16s + 8hf + [0,8)
-  bf16x8 qf[KS];
-  if (qr < L) {
-    const bf16x8* p = reinterpret_cast<const bf16x8*>(qg + static_cast<size_t>(qr) * rs + 8 * hf);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = p[2 * s];
-  } else {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
-  }
-  if (a.qsign != 1) {
-    const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
-  }
-
+  bf16x8 qf[KS];  // Q fragments, read from LDS once the Q tile has arrived
   const int kend = a.causal ? min(L, q0 + BM) : L;
   const int ntiles = (kend + BN - 1) / BN;
   const int nsteps = (kend + SK - 1) / SK;
@@ -349,10 +334,39 @@ void attn_fwd_bf16(KernelArgs a) {
   constexpr int N2 = 2 * NSTEP;
   auto issue_phase = [&](int t) { return max(N2 * t - 4, N2 * (t - TL::kStages + 1) + 2); };
   int t_issue = 0, t_wait = 0;
+  // The workgroup's Q tile goes to the last stage by LDS DMA as well (whole rows,
+  // 16 bytes per lane; rows past the segment end clamped), together with the first
+  // K/V tile.  That stage receives its first tile (tile kStages-1) no earlier than
+  // phase 2 (the staging rule below), after barriers that follow every wave's reads
+  // of its Q fragments.
+  constexpr int QDMA = BM * D / 8 / 64;
+  static_assert(QDMA % TL::kWaves == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  __bf16* ql = lds + (TL::kStages - 1) * TL::kStageElems;
+#pragma unroll
+  for (int u = 0; u < QDMA / TL::kWaves; ++u) {
+    const int i = wave + TL::kWaves * u;
+    const int slot = i * 64 + lane;
+    dma16(qg + static_cast<size_t>(min(q0 + slot / (D / 8), L - 1)) * rs + (slot % (D / 8)) * 8,
+          __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
+  }
   while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++);
   while (t_wait < ntiles && N2 * t_wait - 2 < 0) ++t_wait;
   dma_wait();
   __syncthreads();
+
+  // ---- Q fragments (B operand of S^T): lane holds query qr, channels 16s + 8hf + [0,8)
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(ql + (wave * 32 + n) * D + 16 * s + 8 * hf);
+  if (qr >= L) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  if (a.qsign != 1) {
+    const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
+  }
   auto stage_begin = [&](int p) {
     if (t_issue < ntiles && issue_phase(t_issue) == p) issue_tile(t_issue++);
   };
