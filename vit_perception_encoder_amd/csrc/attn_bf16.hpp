@@ -195,7 +195,7 @@ void attn_fwd_bf16(KernelArgs a) {
     v_row[u] = slot / (D / 8);
     v_off[u] = (slot % (D / 8)) * 8;
   }
-  auto issue_tile = [&](int t) {
+  auto issue_tile = [&](int t, int part) {  // part: 1 = K, 2 = V, 3 = both
     const int kt0 = t * BN;
     const int last = L - 1 - kt0;  // last valid row of this tile (>= 0)
     const __bf16* kb = kg + static_cast<size_t>(kt0) * rs;
@@ -205,7 +205,7 @@ void attn_fwd_bf16(KernelArgs a) {
 #pragma unroll
     for (int u = 0; u < KDMA_W; ++u) {
       const int i = wave + TL::kWaves * u;
-      if (KDMA % TL::kWaves == 0 || i < KDMA) {
+      if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA)) {
         if (k_row[u] >= 0)
           dma16(kb + static_cast<size_t>(min(k_row[u], last)) * rs + k_off[u],
                 __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
@@ -214,7 +214,7 @@ void attn_fwd_bf16(KernelArgs a) {
 #pragma unroll
     for (int u = 0; u < VDMA_W; ++u) {
       const int i = wave + TL::kWaves * u;
-      if (VDMA % TL::kWaves == 0 || i < VDMA)
+      if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
         dma16(vb + static_cast<size_t>(min(v_row[u], last)) * rs + v_off[u],
               __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
     }
@@ -349,7 +349,10 @@ void attn_fwd_bf16(KernelArgs a) {
     dma16(qg + static_cast<size_t>(min(q0 + slot / (D / 8), L - 1)) * rs + (slot % (D / 8)) * 8,
           __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
   }
-  while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++);
+  while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++, 3);
+  // With three stages a tile's V goes one phase after its K (spreading the DMA issue
+  // over two phases); both are waited for at the same phase end.
+  int v_pending = -1;
   while (t_wait < ntiles && N2 * t_wait - 2 < 0) ++t_wait;
   dma_wait();
   __syncthreads();
@@ -368,7 +371,19 @@ void attn_fwd_bf16(KernelArgs a) {
     for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
   }
   auto stage_begin = [&](int p) {
-    if (t_issue < ntiles && issue_phase(t_issue) == p) issue_tile(t_issue++);
+    if (v_pending >= 0) {
+      issue_tile(v_pending, 2);
+      v_pending = -1;
+    }
+    if (t_issue < ntiles && issue_phase(t_issue) == p) {
+      if (TL::kStages >= 3) {
+        issue_tile(t_issue, 1);
+        v_pending = t_issue;
+      } else {
+        issue_tile(t_issue, 3);
+      }
+      ++t_issue;
+    }
   };
   auto stage_end = [&](int p) {
     if (t_wait < ntiles && N2 * t_wait - 2 == p) {
