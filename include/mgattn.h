@@ -52,8 +52,10 @@ typedef enum {
   MGATTN_ERR_SCALE = -9,     /* scale is NaN or infinite, or causal is not 0 or 1 */
   MGATTN_ERR_LAUNCH = -10,   /* the HIP runtime reported an error for the launch */
   MGATTN_ERR_DEVICE = -11,   /* the current device is not a gfx950 GPU */
-  MGATTN_ERR_SIZE = -12      /* a segment spans >= 2^31 bytes (len*H*d*element size),
+  MGATTN_ERR_SIZE = -12,     /* a segment spans >= 2^31 bytes (len*ld*element size),
                                 or a launch would need more than 2^31-1 workgroups */
+  MGATTN_ERR_STRIDE = -13    /* a leading dimension (mgattn_dense_strided) is below H*d,
+                                above 2^31-1, or not a multiple of 16 bytes */
 } mgattn_status;
 
 /*
@@ -89,6 +91,28 @@ typedef enum {
 int mgattn_dense(const void* q, const void* k, const void* v, void* out,
                  const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
                  int causal, int dtype, void* stream);
+
+/*
+ * mgattn_dense_strided: mgattn_dense on tensors whose consecutive tokens are ld
+ * elements apart (row-major [T, ld], head h of token t at offset t*ld + h*d).  The
+ * motivating layout is the merged projection output the perception encoder carries
+ * (vllm.cpp PR #279: the vision tower's q|k|v projections folded into one qkv
+ * matrix at load time): a [T, 3*H*d] buffer qkv is consumed as
+ *     q = qkv, k = qkv + H*d, v = qkv + 2*H*d, ldq = ldk = ldv = 3*H*d
+ * without splitting it first.  out may be strided too (its other elements are not
+ * written).
+ *
+ *   ldq, ldk, ldv, ldo  leading dimensions in elements: >= H*d, <= 2^31-1, and a
+ *                       multiple of 16 bytes (8 bf16 or 4 f32 elements).
+ *   q, k, v             may overlap each other (they are only read).  out must not
+ *                       overlap the span [x, x + ((T-1)*ldx + H*d) elements) of any input.
+ * Every other argument, the return value and the stream semantics are those of
+ * mgattn_dense; mgattn_dense(...) is mgattn_dense_strided with all four = H*d.
+ */
+int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out,
+                         int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                         const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
+                         int causal, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* mgattn_strerror(int status);

@@ -111,6 +111,43 @@ def test_segment_too_large(lib):
     assert _call([0, 1 << 21], o=0x10_0000_0000) == -12
 
 
+def _call_strided(ld, cu=(0, 64, 200), H=16, d=96, dtype=1, q=Q, k=K, v=V, o=O):
+    ldq, ldk, ldv, ldo = ld
+    return mg.mgattn_dense_strided(q, k, v, o, ldq, ldk, ldv, ldo, list(cu), len(cu) - 1, H, d, 0.1, 0, dtype,
+                                   None, check=False)
+
+
+@pytest.mark.parametrize("ld,dtype", [
+    ((1535, 1536, 1536, 1536), 1),           # below H*d
+    ((1536, 1536, 1536, 1540), 1),           # 1540 bf16 = 3080 bytes: not a multiple of 16
+    ((1536, 1536, 1538, 1536), 0),           # f32: 1538 * 4 bytes is not a multiple of 16
+    ((1536, 1536, 1536, 1 << 31), 1),        # above 2^31 - 1
+])
+def test_stride_refusals(lib, ld, dtype):
+    assert _call_strided(ld, dtype=dtype) == -13
+
+
+def test_strided_alias_spans(lib):
+    """Merged q|k|v views of one [T, 3*H*d] buffer may overlap each other; out may
+    not reach into any input's span [x, x + ((T-1)*ld + H*d) elements)."""
+    T, row = 200, 1536
+    base = 0x1000000
+    ld3 = 3 * row
+    q, k, v = base, base + 2 * row, base + 4 * row
+    span = ((T - 1) * ld3 + row) * 2
+    # (an out placed past every span is accepted: covered by the GPU merged-QKV test,
+    # since an accepted call here would launch on these fake addresses)
+    for o in (v + span - 16, q + 2 * row * 3, k + 16):
+        assert mg.mgattn_dense_strided(q, k, v, o, ld3, ld3, ld3, row, [0, 64, T], 2, 16, 96, 0.1, 0, 1,
+                                       None, check=False) == -7
+
+
+def test_strided_segment_too_large(lib):
+    # 2^19 tokens at a leading dimension of 3*1536 bf16 spans 4.5 GiB: refused by name
+    ld3 = 3 * 1536
+    assert _call_strided((ld3, ld3, ld3, 1536), cu=(0, 1 << 19), o=0x100_0000_0000) == -12
+
+
 def _expected_tiles(cu, H, bm):
     out = set()
     for g in range(len(cu) - 1):

@@ -64,6 +64,7 @@ struct KernelArgs {
   int32_t causal;
   float c;        // |scale| * log2(e), or 1 when scale == 0 (always > 0)
   int32_t qsign;  // sign of scale: Q is multiplied by +1, -1 or 0 in registers (exact)
+  int32_t ldq, ldk, ldv, ldo;  // elements between consecutive tokens of q, k, v, out
   SegTable table;
 };
 
@@ -153,12 +154,14 @@ void attn_fwd_bf16(KernelArgs a) {
   if (!tile.valid) return;
   const int L = a.table.len[tile.slot];
   const int q0 = tile.q0;
-  const int rs = a.H * D;  // elements between consecutive tokens
-  const size_t base = (static_cast<size_t>(a.table.start[tile.slot]) * a.H + tile.head) * D;
-  const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + base;
-  const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + base;
-  const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + base;
-  __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + base;
+  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D.
+  const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + t0 * a.ldq + hoff;
+  const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + t0 * a.ldk + hoff;
+  const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + t0 * a.ldv + hoff;
+  __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + t0 * a.ldo + hoff;
+  const int ldk = a.ldk, ldv = a.ldv;
 
   const int tid = threadIdx.x;
   // wave index, marked wave-uniform so branches on it are scalar
@@ -198,8 +201,8 @@ void attn_fwd_bf16(KernelArgs a) {
   auto issue_tile = [&](int t, int part) {  // part: 1 = K, 2 = V, 3 = both
     const int kt0 = t * BN;
     const int last = L - 1 - kt0;  // last valid row of this tile (>= 0)
-    const __bf16* kb = kg + static_cast<size_t>(kt0) * rs;
-    const __bf16* vb = vg + static_cast<size_t>(kt0) * rs;
+    const __bf16* kb = kg + static_cast<size_t>(kt0) * ldk;
+    const __bf16* vb = vg + static_cast<size_t>(kt0) * ldv;
     __bf16* kl = lds + (t % TL::kStages) * TL::kStageElems;
     __bf16* vl = kl + TL::kKElems;
 #pragma unroll
@@ -207,7 +210,7 @@ void attn_fwd_bf16(KernelArgs a) {
       const int i = wave + TL::kWaves * u;
       if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA)) {
         if (k_row[u] >= 0)
-          dma16(kb + static_cast<size_t>(min(k_row[u], last)) * rs + k_off[u],
+          dma16(kb + static_cast<size_t>(min(k_row[u], last)) * ldk + k_off[u],
                 __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
       }
     }
@@ -215,7 +218,7 @@ void attn_fwd_bf16(KernelArgs a) {
     for (int u = 0; u < VDMA_W; ++u) {
       const int i = wave + TL::kWaves * u;
       if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
-        dma16(vb + static_cast<size_t>(min(v_row[u], last)) * rs + v_off[u],
+        dma16(vb + static_cast<size_t>(min(v_row[u], last)) * ldv + v_off[u],
               __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
     }
   };
@@ -346,7 +349,7 @@ void attn_fwd_bf16(KernelArgs a) {
   for (int u = 0; u < QDMA / TL::kWaves; ++u) {
     const int i = wave + TL::kWaves * u;
     const int slot = i * 64 + lane;
-    dma16(qg + static_cast<size_t>(min(q0 + slot / (D / 8), L - 1)) * rs + (slot % (D / 8)) * 8,
+    dma16(qg + static_cast<size_t>(min(q0 + slot / (D / 8), L - 1)) * a.ldq + (slot % (D / 8)) * 8,
           __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
   }
   while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++, 3);
@@ -489,7 +492,7 @@ void attn_fwd_bf16(KernelArgs a) {
     const int cidx = u * 64 + lane;
     const int row = cidx / CH;
     if (qmin + row < L)
-      *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(qmin + row) * rs + (cidx % CH) * 8) = piece_val[u];
+      *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(qmin + row) * a.ldo + (cidx % CH) * 8) = piece_val[u];
   }
 }
 

@@ -52,12 +52,13 @@ void attn_fwd_f32(KernelArgs a) {
   if (!tile.valid) return;
   const int L = a.table.len[tile.slot];
   const int q0 = tile.q0;
-  const int rs = a.H * D;
-  const size_t base = (static_cast<size_t>(a.table.start[tile.slot]) * a.H + tile.head) * D;
-  const float* __restrict__ qg = static_cast<const float*>(a.q) + base;
-  const float* __restrict__ kg = static_cast<const float*>(a.k) + base;
-  const float* __restrict__ vg = static_cast<const float*>(a.v) + base;
-  float* __restrict__ og = static_cast<float*>(a.o) + base;
+  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D.
+  const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const float* __restrict__ qg = static_cast<const float*>(a.q) + t0 * a.ldq + hoff;
+  const float* __restrict__ kg = static_cast<const float*>(a.k) + t0 * a.ldk + hoff;
+  const float* __restrict__ vg = static_cast<const float*>(a.v) + t0 * a.ldv + hoff;
+  float* __restrict__ og = static_cast<float*>(a.o) + t0 * a.ldo + hoff;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -70,7 +71,7 @@ void attn_fwd_f32(KernelArgs a) {
   // Q: lane holds query qr, channels hf*HD + [0, HD)
   float qf[HD];
   if (qr < L) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(qg + static_cast<size_t>(qr) * rs + hf * HD);
+    const f32x4* p = reinterpret_cast<const f32x4*>(qg + static_cast<size_t>(qr) * a.ldq + hf * HD);
 #pragma unroll
     for (int j = 0; j < HD / 4; ++j) {
       const f32x4 x = p[j];
@@ -94,8 +95,8 @@ void attn_fwd_f32(KernelArgs a) {
       const int key = id / (D / 4), part = id % (D / 4);
       const int row = kt0 + key;
       const bool in = row < L;
-      kreg[i] = in ? *reinterpret_cast<const f32x4*>(kg + row * rs + part * 4) : f32x4{};
-      vreg[i] = in ? *reinterpret_cast<const f32x4*>(vg + row * rs + part * 4) : f32x4{};
+      kreg[i] = in ? *reinterpret_cast<const f32x4*>(kg + static_cast<size_t>(row) * a.ldk + part * 4) : f32x4{};
+      vreg[i] = in ? *reinterpret_cast<const f32x4*>(vg + static_cast<size_t>(row) * a.ldv + part * 4) : f32x4{};
     }
   };
   auto store_tile = [&](int buf) {
@@ -187,7 +188,7 @@ void attn_fwd_f32(KernelArgs a) {
 
   const float inv = 1.0f / half_swap_sum(l_run);
   if (qr < L) {
-    float* dst = og + static_cast<size_t>(qr) * rs + 4 * hf;
+    float* dst = og + static_cast<size_t>(qr) * a.ldo + 4 * hf;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll

@@ -12,6 +12,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/mgattn.h"
@@ -59,15 +60,26 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Checks every argument that needs no GPU.  On success, *T_out is the token count.
-int validate(const void* q, const void* k, const void* v, void* out, const int32_t* cu, int n_seg,
-             int H, int d, float scale, int causal, int dtype, int64_t* T_out) {
+// Byte span of a [T rows of H*d elements, leading dimension ld] tensor.
+size_t span_bytes(int64_t T, int64_t ld, int H, int d, int dtype) {
+  return (static_cast<size_t>(T - 1) * static_cast<size_t>(ld) + static_cast<size_t>(H) * d) * elem_size(dtype);
+}
+
+// Checks every argument that needs no GPU.  ld* are the leading dimensions
+// (elements between consecutive tokens).  On success, *T_out is the token count.
+int validate(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
+             int64_t ldo, const int32_t* cu, int n_seg, int H, int d, float scale, int causal, int dtype,
+             int64_t* T_out) {
   if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
   if (!q || !k || !v || !out || !cu) return MGATTN_ERR_NULL;
   if (n_seg < 1) return MGATTN_ERR_SEGMENTS;
   if (H < 1) return MGATTN_ERR_HEADS;
   if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return MGATTN_ERR_SCALE;
+  const int64_t row = static_cast<int64_t>(H) * d;
+  const int64_t align_elems = 16 / static_cast<int64_t>(elem_size(dtype));
+  for (int64_t ld : {ldq, ldk, ldv, ldo})
+    if (ld < row || ld > INT32_MAX || ld % align_elems != 0) return MGATTN_ERR_STRIDE;
   if (cu[0] != 0) return MGATTN_ERR_SEQLENS;
   int64_t max_len = 0;
   for (int g = 0; g < n_seg; ++g) {
@@ -77,14 +89,15 @@ int validate(const void* q, const void* k, const void* v, void* out, const int32
   }
   const int64_t T = cu[n_seg];
   if (T <= 0) return MGATTN_ERR_SEQLENS;
-  // per-segment element offsets are 32-bit inside the kernels
-  if (max_len * static_cast<int64_t>(H) * d * static_cast<int64_t>(elem_size(dtype)) > INT32_MAX)
-    return MGATTN_ERR_SIZE;
+  // the workgroup's element offsets inside one segment stay below 2^31 bytes
+  const int64_t ld_max = std::max(std::max(ldq, ldk), std::max(ldv, ldo));
+  if (max_len * ld_max * static_cast<int64_t>(elem_size(dtype)) > INT32_MAX) return MGATTN_ERR_SIZE;
   if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
         reinterpret_cast<uintptr_t>(out)) & 15u) != 0)
     return MGATTN_ERR_ALIGN;
-  const size_t bytes = static_cast<size_t>(T) * H * d * elem_size(dtype);
-  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+  const size_t bo = span_bytes(T, ldo, H, d, dtype);
+  if (overlaps(out, bo, q, span_bytes(T, ldq, H, d, dtype)) || overlaps(out, bo, k, span_bytes(T, ldk, H, d, dtype)) ||
+      overlaps(out, bo, v, span_bytes(T, ldv, H, d, dtype)))
     return MGATTN_ERR_ALIAS;
   *T_out = T;
   return MGATTN_OK;
@@ -120,10 +133,11 @@ int launch_all(Kern kern, int threads, const std::vector<Launch>& plan, KernelAr
 
 extern "C" {
 
-int mgattn_dense(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,
-                 int n_seg, int H, int d, float scale, int causal, int dtype, void* stream) {
+int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk,
+                         int64_t ldv, int64_t ldo, const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
+                         int causal, int dtype, void* stream) {
   int64_t T = 0;
-  const int st = validate(q, k, v, out, cu_seqlens, n_seg, H, d, scale, causal, dtype, &T);
+  const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens, n_seg, H, d, scale, causal, dtype, &T);
   if (st != MGATTN_OK) return st;
   std::vector<Launch> plan;
   if (!make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
@@ -137,6 +151,10 @@ int mgattn_dense(const void* q, const void* k, const void* v, void* out, const i
   args.o = out;
   args.H = H;
   args.causal = causal;
+  args.ldq = static_cast<int32_t>(ldq);
+  args.ldk = static_cast<int32_t>(ldk);
+  args.ldv = static_cast<int32_t>(ldv);
+  args.ldo = static_cast<int32_t>(ldo);
   // c = |scale| * log2(e) multiplies the scores inside exp2; the sign of scale goes
   // into Q (exact).  For scale == 0 the scores vanish (Q * 0) and c = 1 keeps masked
   // keys at exp2(-inf) = 0.
@@ -159,6 +177,13 @@ int mgattn_dense(const void* q, const void* k, const void* v, void* out, const i
   return MGATTN_ERR_HEAD_DIM;
 }
 
+int mgattn_dense(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,
+                 int n_seg, int H, int d, float scale, int causal, int dtype, void* stream) {
+  const int64_t row = static_cast<int64_t>(H) * d;
+  return mgattn_dense_strided(q, k, v, out, row, row, row, row, cu_seqlens, n_seg, H, d, scale, causal, dtype,
+                              stream);
+}
+
 const char* mgattn_strerror(int status) {
   switch (status) {
     case MGATTN_OK: return "ok";
@@ -175,6 +200,8 @@ const char* mgattn_strerror(int status) {
     case MGATTN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case MGATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case MGATTN_ERR_SIZE: return "a segment spans more than 2^31 bytes, or the grid is too large";
+    case MGATTN_ERR_STRIDE:
+      return "a leading dimension is below H*d, above 2^31-1, or not a multiple of 16 bytes";
   }
   return "unknown mgattn status";
 }

@@ -22,10 +22,10 @@ STATUS_NAMES = {
     0: "MGATTN_OK", -1: "MGATTN_ERR_NULL", -2: "MGATTN_ERR_DTYPE", -3: "MGATTN_ERR_HEAD_DIM",
     -4: "MGATTN_ERR_HEADS", -5: "MGATTN_ERR_SEQLENS", -6: "MGATTN_ERR_SEGMENTS",
     -7: "MGATTN_ERR_ALIAS", -8: "MGATTN_ERR_ALIGN", -9: "MGATTN_ERR_SCALE",
-    -10: "MGATTN_ERR_LAUNCH", -11: "MGATTN_ERR_DEVICE", -12: "MGATTN_ERR_SIZE",
+    -10: "MGATTN_ERR_LAUNCH", -11: "MGATTN_ERR_DEVICE", -12: "MGATTN_ERR_SIZE", -13: "MGATTN_ERR_STRIDE",
 }
 
-EXPORTS = ["mgattn_dense", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
+EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
            "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_version"]
 
 
@@ -51,6 +51,8 @@ def load_library(path: str | os.PathLike | None = None):
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.mgattn_dense.restype = i32
     lib.mgattn_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp]
+    lib.mgattn_dense_strided.restype = i32
+    lib.mgattn_dense_strided.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, i32, i32, f32, i32, i32, vp]
     lib.mgattn_strerror.restype = ctypes.c_char_p
     lib.mgattn_strerror.argtypes = [i32]
     lib.mgattn_dense_supported.restype = i32
@@ -105,6 +107,23 @@ def mgattn_dense(q, k, v, out, cu_seqlens: Sequence[int], n_seg: int, H: int, d:
                           int(H), int(d), float(scale), int(causal), int(dtype), _stream(stream))
     if check and st != 0:
         raise MgattnError(st)
+    return st
+
+
+def mgattn_dense_strided(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu_seqlens: Sequence[int],
+                         n_seg: int, H: int, d: int, scale: float, causal: int, dtype: int, stream=None,
+                         check: bool = True) -> int:
+    """mgattn_dense on row-strided tensors (see mgattn_dense_strided in include/mgattn.h);
+    ld* are leading dimensions in elements.  For torch views, pass e.g. ``t.stride(0)``."""
+    lib = load_library()
+    cu, ncu = _cu_array(cu_seqlens)
+    if ncu < n_seg + 1:
+        raise ValueError(f"cu_seqlens has {ncu} entries, n_seg={n_seg} needs {n_seg + 1}")
+    st = lib.mgattn_dense_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
+                                  ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), float(scale),
+                                  int(causal), int(dtype), _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_dense_strided")
     return st
 
 
