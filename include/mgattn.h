@@ -54,8 +54,10 @@ typedef enum {
   MGATTN_ERR_DEVICE = -11,   /* the current device is not a gfx950 GPU */
   MGATTN_ERR_SIZE = -12,     /* a segment spans >= 2^31 bytes (len*ld*element size),
                                 or a launch would need more than 2^31-1 workgroups */
-  MGATTN_ERR_STRIDE = -13    /* a leading dimension (mgattn_dense_strided) is below H*d,
-                                above 2^31-1, or not a multiple of 16 bytes */
+  MGATTN_ERR_STRIDE = -13,   /* a leading dimension is below H*d, above 2^31-1, or not
+                                a multiple of 16 bytes (also: a bad row_bytes) */
+  MGATTN_ERR_GRID = -14      /* a patch grid is empty, more than 64 images, a window
+                                below its minimum, or a flag is not 0 or 1 */
 } mgattn_status;
 
 /*
@@ -146,6 +148,57 @@ int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
                       int64_t* grids, int max_launches);
 int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
                       int launch, int64_t block, int32_t* seg_head_q0);
+
+/*
+ * Token order of the perception encoder's patch grids.
+ *
+ * A batch is n_img images; grids[2i], grids[2i+1] are image i's patch-grid height
+ * and width (gh, gw >= 1, 1 <= n_img <= 64).  In raster order, image i's tokens
+ * follow those of images < i, row-major (token y*gw + x).  Window layers attend
+ * within win x win blocks of patches (vllm.cpp issue #1545, second comment: the
+ * vision tower's sparse permutation cuts 32x32 = 1024-patch windows); in window
+ * order each image's tokens are regrouped block by block so that every block is a
+ * contiguous segment.  The pages do not state the block walk order or the order
+ * inside a block; this library takes row-major over the blocks (blocks at the right
+ * and bottom edges clipped to the grid) and row-major inside a block.  The order
+ * inside a block does not change the attention output; the block order fixes the
+ * sequence of segments.
+ */
+
+/* Segments of the window layers: writes the n_seg+1 prefix sums of the window
+ * sizes, in window order, to cu_seqlens (host) and returns n_seg.  With cu_seqlens
+ * NULL, only returns n_seg; if max_seg < n_seg, returns MGATTN_ERR_SIZE.  A window at
+ * least as large as every grid gives one segment per image (the full-attention
+ * layers).  Pure host arithmetic. */
+int mgattn_window_segments(const int32_t* grids, int n_img, int win, int32_t* cu_seqlens, int max_seg);
+
+/* Enqueue on `stream` the permutation of T = sum(gh*gw) rows of row_bytes bytes
+ * (row_bytes a multiple of 16): inverse == 0 gathers src (raster order) into dst
+ * (window order of window win); inverse == 1 scatters src (window order) back into
+ * dst (raster order), as the tower does before its final LayerNorm (vllm.cpp PR
+ * #279, vision-tower commit).  src and dst are caller-owned device buffers of
+ * T*row_bytes bytes, 16-byte aligned, not overlapping.  Any element type: rows are
+ * moved as bytes. */
+int mgattn_window_permute(const void* src, void* dst, int64_t row_bytes, const int32_t* grids, int n_img,
+                          int win, int inverse, void* stream);
+
+/* Enqueue on `stream` the 2D rotary position embedding of the vision tower (vllm.cpp
+ * PR #279, vision-tower commits: width-first order, 1-based positions), in place on
+ * x: T = sum(gh*gw) token rows with leading dimension ldx elements, each holding H
+ * heads of d channels (head h of token t at t*ldx + h*d), in `dtype`.  Tokens are in
+ * raster order if win == 0, in the window order of window win (as produced by
+ * mgattn_window_permute) if win > 0; the position of a token is that of its patch.
+ * The pages name the convention without a formula; the reading taken:
+ *   for a patch at row y, column x, and each head:
+ *     channels [0, d/2) rotate with position x + 1, channels [d/2, d) with y + 1;
+ *     inside a half, pair (2i, 2i+1) is multiplied, as the complex number
+ *     c_2i + i*c_2i+1, by exp(i * pos * theta^(-4i/d)),  i = 0 .. d/4 - 1.
+ * Angles are formed in f32 (pos * f32(theta^(-4i/d)), theta^(-4i/d) computed in
+ * double on the host) and rotated with f32 sincos; bf16 results are rounded to
+ * nearest even.  d is a multiple of 16 in [16, 128]; theta > 1 and finite (the
+ * tower's value is not on the pages; 10000 is the customary base). */
+int mgattn_rope2d(void* x, int64_t ldx, const int32_t* grids, int n_img, int win, int H, int d, float theta,
+                  int dtype, void* stream);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int mgattn_version(void);

@@ -19,6 +19,7 @@
 #include "attn_bf16.hpp"
 #include "attn_f32.hpp"
 #include "plan.hpp"
+#include "window_rope.hpp"
 
 using namespace mgattn;
 
@@ -129,6 +130,33 @@ int launch_all(Kern kern, int threads, const std::vector<Launch>& plan, KernelAr
   return MGATTN_OK;
 }
 
+// Image table of a batch of patch grids (grids: n_img pairs {gh, gw}).
+int make_images(const int32_t* grids, int n_img, ImageTable* tb) {
+  if (!grids) return MGATTN_ERR_NULL;
+  if (n_img < 1 || n_img > kMaxImages) return MGATTN_ERR_GRID;
+  memset(tb, 0, sizeof *tb);
+  tb->n = n_img;
+  int64_t t = 0;
+  for (int i = 0; i < n_img; ++i) {
+    const int32_t gh = grids[2 * i], gw = grids[2 * i + 1];
+    if (gh < 1 || gw < 1) return MGATTN_ERR_GRID;
+    tb->start[i] = static_cast<int32_t>(t);
+    tb->gh[i] = gh;
+    tb->gw[i] = gw;
+    t += static_cast<int64_t>(gh) * gw;
+    if (t > INT32_MAX) return MGATTN_ERR_SIZE;
+  }
+  tb->start[n_img] = static_cast<int32_t>(t);
+  return MGATTN_OK;
+}
+
+int blocks_for(int64_t items, unsigned* grid) {
+  const int64_t b = (items + 255) / 256;
+  if (b < 1 || b > INT32_MAX) return MGATTN_ERR_SIZE;
+  *grid = static_cast<unsigned>(b);
+  return MGATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +228,8 @@ const char* mgattn_strerror(int status) {
     case MGATTN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case MGATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case MGATTN_ERR_SIZE: return "a segment spans more than 2^31 bytes, or the grid is too large";
+    case MGATTN_ERR_GRID:
+      return "a patch grid is empty, more than 64 images, a window below 1, or inverse not 0 or 1";
     case MGATTN_ERR_STRIDE:
       return "a leading dimension is below H*d, above 2^31-1, or not a multiple of 16 bytes";
   }
@@ -254,6 +284,95 @@ int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
   seg_head_q0[1] = t.head;
   seg_head_q0[2] = t.q0;
   return 1;
+}
+
+int mgattn_window_segments(const int32_t* grids, int n_img, int win, int32_t* cu_seqlens, int max_seg) {
+  ImageTable tb;
+  const int st = make_images(grids, n_img, &tb);
+  if (st != MGATTN_OK) return st;
+  if (win < 1) return MGATTN_ERR_GRID;
+  int64_t n_seg = 0;
+  for (int i = 0; i < n_img; ++i)
+    n_seg += static_cast<int64_t>((tb.gh[i] + win - 1) / win) * ((tb.gw[i] + win - 1) / win);
+  if (n_seg > INT32_MAX - 1) return MGATTN_ERR_SIZE;
+  if (!cu_seqlens) return static_cast<int>(n_seg);
+  if (max_seg < n_seg) return MGATTN_ERR_SIZE;
+  int g = 0;
+  cu_seqlens[0] = 0;
+  for (int i = 0; i < n_img; ++i) {
+    const int gh = tb.gh[i], gw = tb.gw[i];
+    for (int y0 = 0; y0 < gh; y0 += win)
+      for (int x0 = 0; x0 < gw; x0 += win) {
+        cu_seqlens[g + 1] = cu_seqlens[g] + std::min(win, gh - y0) * std::min(win, gw - x0);
+        ++g;
+      }
+  }
+  return static_cast<int>(n_seg);
+}
+
+int mgattn_window_permute(const void* src, void* dst, int64_t row_bytes, const int32_t* grids, int n_img,
+                          int win, int inverse, void* stream) {
+  if (!src || !dst) return MGATTN_ERR_NULL;
+  ImageTable tb;
+  const int st = make_images(grids, n_img, &tb);
+  if (st != MGATTN_OK) return st;
+  if (win < 1 || (inverse != 0 && inverse != 1)) return MGATTN_ERR_GRID;
+  if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes / 16 > INT32_MAX) return MGATTN_ERR_STRIDE;
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0) return MGATTN_ERR_ALIGN;
+  const int64_t T = tb.start[n_img];
+  const size_t bytes = static_cast<size_t>(T) * static_cast<size_t>(row_bytes);
+  if (overlaps(src, bytes, dst, bytes)) return MGATTN_ERR_ALIAS;
+  const int64_t pieces = T * (row_bytes / 16);
+  unsigned grid = 0;
+  if (blocks_for(pieces, &grid) != MGATTN_OK) return MGATTN_ERR_SIZE;
+  if (!device_ok()) return MGATTN_ERR_DEVICE;
+  const uint4* s = static_cast<const uint4*>(src);
+  uint4* d = static_cast<uint4*>(dst);
+  int32_t ppr = static_cast<int32_t>(row_bytes / 16), w = win, inv = inverse;
+  int64_t total = pieces;
+  void* params[] = {&s, &d, &ppr, &w, &inv, &total, &tb};
+  return hipLaunchKernel(reinterpret_cast<const void*>(window_permute_kernel), dim3(grid), dim3(256), params, 0,
+                         static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MGATTN_OK
+             : MGATTN_ERR_LAUNCH;
+}
+
+int mgattn_rope2d(void* x, int64_t ldx, const int32_t* grids, int n_img, int win, int H, int d, float theta,
+                  int dtype, void* stream) {
+  if (!x) return MGATTN_ERR_NULL;
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  ImageTable tb;
+  const int st = make_images(grids, n_img, &tb);
+  if (st != MGATTN_OK) return st;
+  if (win < 0) return MGATTN_ERR_GRID;
+  if (H < 1) return MGATTN_ERR_HEADS;
+  if (d < 16 || d > 128 || d % 16 != 0) return MGATTN_ERR_HEAD_DIM;
+  if (!(theta > 1.0f) || !isfinite(theta)) return MGATTN_ERR_SCALE;
+  const int64_t row = static_cast<int64_t>(H) * d;
+  if (ldx < row || ldx > INT32_MAX || ldx % (16 / static_cast<int64_t>(elem_size(dtype))) != 0)
+    return MGATTN_ERR_STRIDE;
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return MGATTN_ERR_ALIGN;
+  RopeArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.ld = ldx;
+  a.H = H;
+  a.d = d;
+  a.win = win;
+  a.pieces = static_cast<int32_t>(row * static_cast<int64_t>(elem_size(dtype)) / 16);
+  for (int i = 0; i < d / 4; ++i)
+    a.inv_freq[i] = static_cast<float>(pow(static_cast<double>(theta), -4.0 * i / d));
+  a.tb = tb;
+  const int64_t pieces = static_cast<int64_t>(tb.start[n_img]) * a.pieces;
+  unsigned grid = 0;
+  if (blocks_for(pieces, &grid) != MGATTN_OK) return MGATTN_ERR_SIZE;
+  if (!device_ok()) return MGATTN_ERR_DEVICE;
+  void* params[] = {&a, const_cast<int64_t*>(&pieces)};
+  const void* kern = dtype == MGATTN_BF16 ? reinterpret_cast<const void*>(rope2d_kernel<__bf16>)
+                                          : reinterpret_cast<const void*>(rope2d_kernel<float>);
+  return hipLaunchKernel(kern, dim3(grid), dim3(256), params, 0, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MGATTN_OK
+             : MGATTN_ERR_LAUNCH;
 }
 
 int mgattn_version(void) { return kVersion; }

@@ -23,10 +23,12 @@ STATUS_NAMES = {
     -4: "MGATTN_ERR_HEADS", -5: "MGATTN_ERR_SEQLENS", -6: "MGATTN_ERR_SEGMENTS",
     -7: "MGATTN_ERR_ALIAS", -8: "MGATTN_ERR_ALIGN", -9: "MGATTN_ERR_SCALE",
     -10: "MGATTN_ERR_LAUNCH", -11: "MGATTN_ERR_DEVICE", -12: "MGATTN_ERR_SIZE", -13: "MGATTN_ERR_STRIDE",
+    -14: "MGATTN_ERR_GRID",
 }
 
 EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
-           "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_version"]
+           "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
+           "mgattn_window_permute", "mgattn_rope2d", "mgattn_version"]
 
 
 class MgattnError(RuntimeError):
@@ -65,6 +67,12 @@ def load_library(path: str | os.PathLike | None = None):
     lib.mgattn_dense_plan.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32]
     lib.mgattn_dense_tile.restype = i32
     lib.mgattn_dense_tile.argtypes = [vp, i32, i32, i32, i32, i32, i32, i64, vp]
+    lib.mgattn_window_segments.restype = i32
+    lib.mgattn_window_segments.argtypes = [vp, i32, i32, vp, i32]
+    lib.mgattn_window_permute.restype = i32
+    lib.mgattn_window_permute.argtypes = [vp, vp, i64, vp, i32, i32, i32, vp]
+    lib.mgattn_rope2d.restype = i32
+    lib.mgattn_rope2d.argtypes = [vp, i64, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.mgattn_version.restype = i32
     lib.mgattn_version.argtypes = []
     if path is None:
@@ -167,6 +175,51 @@ def mgattn_dense_tile(cu_seqlens, n_seg: int, H: int, d: int, dtype: int, causal
     if r < 0:
         raise MgattnError(r, "mgattn_dense_tile")
     return (int(out[0]), int(out[1]), int(out[2])) if r == 1 else None
+
+
+def _grid_array(grids):
+    """[(gh, gw), ...] -> int32[2*n] (host)."""
+    flat = [int(v) for g in grids for v in g]
+    return (ctypes.c_int32 * max(len(flat), 1))(*flat), len(flat) // 2
+
+
+def mgattn_window_segments(grids, win: int) -> list[int]:
+    """cu_seqlens of the window layers for patch grids [(gh, gw), ...] (raises on refusal)."""
+    lib = load_library()
+    g, n_img = _grid_array(grids)
+    gp = ctypes.cast(g, ctypes.c_void_p)
+    n = lib.mgattn_window_segments(gp, n_img, int(win), None, 0)
+    if n < 0:
+        raise MgattnError(n, "mgattn_window_segments")
+    cu = (ctypes.c_int32 * (n + 1))()
+    r = lib.mgattn_window_segments(gp, n_img, int(win), ctypes.cast(cu, ctypes.c_void_p), n)
+    if r < 0:
+        raise MgattnError(r, "mgattn_window_segments")
+    return [int(x) for x in cu]
+
+
+def mgattn_window_permute(src, dst, row_bytes: int, grids, win: int, inverse: int, stream=None,
+                          check: bool = True) -> int:
+    """Gather rows into window order (inverse=0) or scatter them back (inverse=1)."""
+    lib = load_library()
+    g, n_img = _grid_array(grids)
+    st = lib.mgattn_window_permute(_ptr(src), _ptr(dst), int(row_bytes), ctypes.cast(g, ctypes.c_void_p), n_img,
+                                   int(win), int(inverse), _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_window_permute")
+    return st
+
+
+def mgattn_rope2d(x, ldx: int, grids, win: int, H: int, d: int, theta: float, dtype: int, stream=None,
+                  check: bool = True) -> int:
+    """In-place 2D rotary embedding of x (token rows of leading dimension ldx)."""
+    lib = load_library()
+    g, n_img = _grid_array(grids)
+    st = lib.mgattn_rope2d(_ptr(x), int(ldx), ctypes.cast(g, ctypes.c_void_p), n_img, int(win), int(H), int(d),
+                           float(theta), int(dtype), _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_rope2d")
+    return st
 
 
 def mgattn_version() -> int:
