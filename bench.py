@@ -37,6 +37,8 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "attention TFLOP/s (%bf16 MFMA peak) + ms per 50-layer tower attn @4096 tok"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published 2.5 PFLOP/s): 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published 8 TB/s)
+THETA = 10000.0
 KERNEL_NAME = "attn_fwd_bf16<96>"
 TRAFFIC_FILE = ROOT / "profiles" / "attn_fwd_bf16_96_tower4096_traffic.json"
 KERNEL_SOURCES = ["vit_perception_encoder_amd/csrc/attn_bf16.hpp", "vit_perception_encoder_amd/csrc/plan.hpp",
@@ -86,6 +88,62 @@ def cpu_baseline(layer_cases):
                   "sample": f"{len(layer_cases)} full-attention layers of the schedule ({names}; each 1 segment x "
                             f"4096 tokens, H=16, d=96, bf16 inputs widened to f64), whole outputs, "
                             f"{flops / 1e9:.1f} GFLOP"}
+
+
+def time_launches(torch, fn, reps: int = 20, warm: int = 3) -> float:
+    """Median milliseconds of fn() (one enqueue on torch's current stream), events
+    around each launch."""
+    for _ in range(warm):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
+def token_path(torch, mg, wl, layers):
+    """The other entry points on the same shapes: the 4096-token full layer read from a
+    merged [T, 3*H*d] qkv buffer, and the HBM-bound token-order kernels (window gather
+    of a [T, H*d] bf16 tensor, 2D RoPE in place on the q and k columns of a merged qkv
+    buffer) at the tower's 64x64 grid and at the 17,408-token ragged batch."""
+    dev = torch.device("cuda:0")
+    H, d = wl.HEADS, wl.HEAD_DIM
+    row = H * d
+    stream = torch.cuda.current_stream()
+    res = {}
+    # merged qkv, full layer 3
+    q, k, v, cu, nseg, flops, _ = layers[3]
+    T = q.shape[0]
+    qkv = torch.cat([q, k, v], dim=1).contiguous()
+    out = torch.empty(T, row, dtype=torch.bfloat16, device=dev)
+    ms = time_launches(torch, lambda: mg.mgattn_dense_strided(
+        qkv[:, :row], qkv[:, row:2 * row], qkv[:, 2 * row:], out, qkv.stride(0), qkv.stride(0), qkv.stride(0),
+        row, cu, nseg, H, d, wl.SCALE, 0, mg.MGATTN_BF16, stream))
+    res["merged_qkv_full_layer_4096"] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                                         "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    for name, grids in (("tower_64x64", [(64, 64)]), ("ragged_17408", [(128, 96), (64, 64), (32, 32)])):
+        T = sum(gh * gw for gh, gw in grids)
+        x = torch.randn(T, row, device=dev).to(torch.bfloat16)
+        y = torch.empty_like(x)
+        ms_g = time_launches(torch, lambda: mg.mgattn_window_permute(x, y, row * 2, grids, 32, 0, stream))
+        moved = 2 * T * row * 2  # read + write
+        qkv3 = torch.randn(T, 3 * row, device=dev).to(torch.bfloat16)
+
+        def rope_qk():
+            for part in (0, 1):
+                mg.mgattn_rope2d(qkv3[:, part * row:(part + 1) * row], qkv3.stride(0), grids, 32, H, d, THETA,
+                                 mg.MGATTN_BF16, stream)
+        ms_r = time_launches(torch, rope_qk)
+        rot = 2 * 2 * T * row * 2  # q and k, read + write
+        res[f"window_gather_{name}"] = {"ms": ms_g, "bytes": moved, "gbs": moved / (ms_g * 1e-3) / 1e9,
+                                        "frac_hbm": moved / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        res[f"rope2d_qk_{name}"] = {"ms": ms_r, "launches": 2, "bytes": rot, "gbs": rot / (ms_r * 1e-3) / 1e9,
+                                    "frac_hbm": rot / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return res
 
 
 def main() -> int:
@@ -195,6 +253,9 @@ def main() -> int:
     full_tf = layers[full_idx[0]][5] / (full_ms * 1e-3) / 1e12
     win_tf = layers[win_idx[0]][5] / (win_ms * 1e-3) / 1e12
 
+    print("[bench] timing the other entry points (merged qkv, window gather, 2D RoPE)", file=sys.stderr, flush=True)
+    token = token_path(torch, mg, wl, layers)
+
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         b = torch.empty_like(a)
@@ -248,6 +309,7 @@ def main() -> int:
             "step_gflop": step_flops / 1e9,
             "wall_s_timed_region": wall,
             "oracle_parity_full_layers_max_abs_err": parity,
+            "token_path": token,
             "kernel_source_sha256": kernel_source_hash(),
         },
     }
