@@ -359,15 +359,16 @@ int mgattn_rope2d(void* x, int64_t ldx, const int32_t* grids, int n_img, int win
   a.H = H;
   a.d = d;
   a.win = win;
-  a.pieces = static_cast<int32_t>(row * static_cast<int64_t>(elem_size(dtype)) / 16);
+  a.pieces = static_cast<int32_t>(static_cast<int64_t>(d) * static_cast<int64_t>(elem_size(dtype)) / 16);
+  a.groups = (H + kRopeHeadGroup - 1) / kRopeHeadGroup;
   for (int i = 0; i < d / 4; ++i)
     a.inv_freq[i] = static_cast<float>(pow(static_cast<double>(theta), -4.0 * i / d));
   a.tb = tb;
-  const int64_t pieces = static_cast<int64_t>(tb.start[n_img]) * a.pieces;
+  int64_t threads = static_cast<int64_t>(tb.start[n_img]) * a.pieces * a.groups;
   unsigned grid = 0;
-  if (blocks_for(pieces, &grid) != MGATTN_OK) return MGATTN_ERR_SIZE;
+  if (blocks_for(threads, &grid) != MGATTN_OK) return MGATTN_ERR_SIZE;
   if (!device_ok()) return MGATTN_ERR_DEVICE;
-  void* params[] = {&a, const_cast<int64_t*>(&pieces)};
+  void* params[] = {&a, &threads};
   const void* kern = dtype == MGATTN_BF16 ? reinterpret_cast<const void*>(rope2d_kernel<__bf16>)
                                           : reinterpret_cast<const void*>(rope2d_kernel<float>);
   return hipLaunchKernel(kern, dim3(grid), dim3(256), params, 0, static_cast<hipStream_t>(stream)) == hipSuccess

@@ -76,64 +76,74 @@ void window_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ ds
   dst[static_cast<int64_t>(to) * pieces_per_row + piece] = src[static_cast<int64_t>(from) * pieces_per_row + piece];
 }
 
+constexpr int kRopeHeadGroup = 4;  // heads per thread: angles computed once for them
+
 struct RopeArgs {
   void* x;
-  int64_t ld;        // elements between consecutive tokens
+  int64_t ld;          // elements between consecutive tokens
   int32_t H, d;
-  int32_t win;       // 0: tokens in raster order; > 0: in window order of this window
-  int32_t pieces;    // 16-byte pieces per token row that hold heads (H*d*elem/16)
+  int32_t win;         // 0: tokens in raster order; > 0: in window order of this window
+  int32_t pieces;      // 16-byte pieces per head (d*elem/16)
+  int32_t groups;      // head groups per token: ceil(H / kRopeHeadGroup)
   float inv_freq[32];  // theta^(-4i/d), i < d/4
   ImageTable tb;
 };
 
-__device__ inline void rotate(float& a, float& b, float pos, float w) {
-  float s, c;
-  sincosf(pos * w, &s, &c);
-  const float a2 = a * c - b * s;
-  const float b2 = a * s + b * c;
-  a = a2;
-  b = b2;
-}
-
-// In-place rotation; one 16-byte piece (8 bf16 or 4 f32 values, whole pairs, inside
-// one half of one head since d/2 is a multiple of 8) per thread.
+// One thread = one 16-byte piece (8 bf16 or 4 f32 values: whole pairs inside one half
+// of a head, since d/2 is a multiple of 8) of one token, for up to kRopeHeadGroup
+// heads: the angles depend on the token and the pair only, so they are computed once
+// and applied to each head of the group.  In place.
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void rope2d_kernel(RopeArgs a, int64_t total_pieces) {
-  constexpr int kPer = 16 / sizeof(T);
+void rope2d_kernel(RopeArgs a, int64_t total_threads) {
+  constexpr int kPer = 16 / sizeof(T);  // values per piece
+  constexpr int kPairs = kPer / 2;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= total_pieces) return;
-  const int t = static_cast<int>(i / a.pieces);
-  const int piece = static_cast<int>(i - static_cast<int64_t>(t) * a.pieces);
+  if (i >= total_threads) return;
+  const int per_token = a.pieces * a.groups;
+  const int t = static_cast<int>(i / per_token);
+  const int rem = static_cast<int>(i - static_cast<int64_t>(t) * per_token);
+  const int grp = rem / a.pieces, piece = rem % a.pieces;
   const int img = image_of(a.tb, t);
   const int p = t - a.tb.start[img];
   const int gw = a.tb.gw[img];
   const int r = a.win > 0 ? window_to_raster(p, a.tb.gh[img], gw, a.win) : p;
-  const float py = static_cast<float>(r / gw + 1), px = static_cast<float>(r % gw + 1);
-  const int c0 = (piece * kPer) % a.d;  // first channel of the piece inside its head
+  const int c0 = piece * kPer;          // first channel of the piece inside its head
   const int half = a.d / 2;
-  const float pos = c0 < half ? px : py;
+  const float pos = static_cast<float>(c0 < half ? r % gw + 1 : r / gw + 1);
   const int i0 = (c0 % half) / 2;       // pair index of the piece's first pair
-  uint4* ptr = reinterpret_cast<uint4*>(static_cast<T*>(a.x) + static_cast<int64_t>(t) * a.ld) + piece;
-  uint4 raw = *ptr;
-  if constexpr (sizeof(T) == 2) {
-    uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float cs[kPairs], sn[kPairs];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xffff0000u);
-      rotate(lo, hi, pos, a.inv_freq[i0 + j]);
-      const __bf16 blo = static_cast<__bf16>(lo), bhi = static_cast<__bf16>(hi);
-      w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, blo)) |
-             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bhi)) << 16);
+  for (int j = 0; j < kPairs; ++j) sincosf(pos * a.inv_freq[i0 + j], &sn[j], &cs[j]);
+  const int h0 = grp * kRopeHeadGroup, h1 = min(a.H, h0 + kRopeHeadGroup);
+  T* row = static_cast<T*>(a.x) + static_cast<int64_t>(t) * a.ld + c0;
+  uint4 raw[kRopeHeadGroup];
+#pragma unroll
+  for (int k = 0; k < kRopeHeadGroup; ++k)
+    if (h0 + k < h1) raw[k] = *reinterpret_cast<const uint4*>(row + static_cast<int64_t>(h0 + k) * a.d);
+#pragma unroll
+  for (int k = 0; k < kRopeHeadGroup; ++k) {
+    if (h0 + k >= h1) break;
+    uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float re = __uint_as_float(w[j] << 16), im = __uint_as_float(w[j] & 0xffff0000u);
+        const __bf16 a2 = static_cast<__bf16>(re * cs[j] - im * sn[j]);
+        const __bf16 b2 = static_cast<__bf16>(re * sn[j] + im * cs[j]);
+        w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a2)) |
+               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) << 16);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float re = __uint_as_float(w[2 * j]), im = __uint_as_float(w[2 * j + 1]);
+        w[2 * j] = __float_as_uint(re * cs[j] - im * sn[j]);
+        w[2 * j + 1] = __float_as_uint(re * sn[j] + im * cs[j]);
+      }
     }
-    raw = uint4{w[0], w[1], w[2], w[3]};
-  } else {
-    float v[4] = {__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z), __uint_as_float(raw.w)};
-    rotate(v[0], v[1], pos, a.inv_freq[i0]);
-    rotate(v[2], v[3], pos, a.inv_freq[i0 + 1]);
-    raw = uint4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    *reinterpret_cast<uint4*>(row + static_cast<int64_t>(h0 + k) * a.d) = uint4{w[0], w[1], w[2], w[3]};
   }
-  *ptr = raw;
 }
 
 }  // namespace mgattn
