@@ -44,7 +44,7 @@ typedef enum {
   MGATTN_ERR_NULL = -1,      /* a required pointer is NULL */
   MGATTN_ERR_DTYPE = -2,     /* dtype is not an mgattn_dtype */
   MGATTN_ERR_HEAD_DIM = -3,  /* head_dim outside mgattn_dense_supported's domain */
-  MGATTN_ERR_HEADS = -4,     /* H < 1 */
+  MGATTN_ERR_HEADS = -4,     /* H < 1 (mgattn_attention_kv: Hkv < 1 or Hq % Hkv != 0) */
   MGATTN_ERR_SEQLENS = -5,   /* cu_seqlens malformed (see mgattn_dense) */
   MGATTN_ERR_SEGMENTS = -6,  /* n_seg < 1 */
   MGATTN_ERR_ALIAS = -7,     /* out overlaps q, k or v */
@@ -56,8 +56,9 @@ typedef enum {
                                 or a launch would need more than 2^31-1 workgroups */
   MGATTN_ERR_STRIDE = -13,   /* a leading dimension is below H*d, above 2^31-1, or not
                                 a multiple of 16 bytes (also: a bad row_bytes) */
-  MGATTN_ERR_GRID = -14      /* a patch grid is empty, more than 64 images, a window
+  MGATTN_ERR_GRID = -14,     /* a patch grid is empty, more than 64 images, a window
                                 below its minimum, or a flag is not 0 or 1 */
+  MGATTN_ERR_WINDOW = -15    /* mgattn_attention_kv: window < 0 */
 } mgattn_status;
 
 /*
@@ -115,6 +116,39 @@ int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out,
                          int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
                          const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
                          int causal, int dtype, void* stream);
+
+/*
+ * mgattn_attention_kv: causal sliding-window attention with grouped key/value heads
+ * over a key/value cache -- the attention of the Muse Glimmer text decoder (mbext
+ * next-steps page, "Architecture / Text decoder": 32 query heads, 2 key/value heads,
+ * head size 128, a repeating [sliding, sliding, sliding, full] pattern with a local
+ * window of 2048 tokens; prefill and incremental decoding with a KV cache).
+ *
+ * n_seq sequences.  Sequence s has Lq = cu_seqlens_q[s+1] - cu_seqlens_q[s] new
+ * queries (rows of q and out) and Lk = cu_seqlens_k[s+1] - cu_seqlens_k[s] >= Lq keys
+ * and values (rows of k and v: the cache, ending with the new tokens' own entries).
+ * Query i of the sequence sits at position p = Lk - Lq + i; for query head h and key
+ * /value head g = h / (Hq / Hkv),
+ *     out[i,h,:] = sum_j softmax_j(scale * <q[i,h,:], k[j,g,:]>) * v[j,g,:]
+ * with j over [max(0, p - window + 1), p] (window == 0: over [0, p]).  The local window
+ * thus holds the query's own key and the window-1 before it; prefill is Lq == Lk,
+ * one-token decoding Lq == 1.
+ *
+ *   q, out   device, [Tq rows, leading dimension ldq / ldo], Hq heads of d channels
+ *            (Tq = cu_seqlens_q[n_seq]); ldq, ldo >= Hq*d.
+ *   k, v     device, [Tk rows, leading dimension ldk / ldv], Hkv heads of d channels
+ *            (Tk = cu_seqlens_k[n_seq]); ldk, ldv >= Hkv*d.
+ *   cu_seqlens_q, cu_seqlens_k   HOST arrays of n_seq+1 int32 (prefix sums as in
+ *            mgattn_dense); a sequence with Lq == 0 does nothing.
+ *   Hq, Hkv  query and key/value heads, Hkv >= 1, Hq a multiple of Hkv.
+ *   window   >= 0 (0: no window, plain causal).
+ * Every other argument, alignment, aliasing rule, return value and the stream
+ * semantics are those of mgattn_dense_strided.
+ */
+int mgattn_attention_kv(const void* q, const void* k, const void* v, void* out,
+                        int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
+                        int Hq, int Hkv, int d, float scale, int window, int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* mgattn_strerror(int status);

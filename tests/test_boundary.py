@@ -206,3 +206,30 @@ def test_plan_causal_puts_last_qtile_first(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         mg.load_library(tmp_path / "missing.so")
+
+
+def _call_kv(cq=(0, 10, 30), ck=(0, 20, 50), Hq=32, Hkv=2, d=128, window=2048, dtype=1, ld=None,
+             q=Q, k=K, v=V, o=O):
+    ldq, ldk, ldv, ldo = ld or (Hq * d, Hkv * d, Hkv * d, Hq * d)
+    return mg.mgattn_attention_kv(q, k, v, o, ldq, ldk, ldv, ldo, list(cq), list(ck), len(cq) - 1, Hq, Hkv, d, 0.1,
+                                  window, dtype, None, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=3), -4), (dict(Hkv=0), -4), (dict(Hq=0), -4),
+    (dict(window=-1), -15),
+    (dict(ck=(0, 5, 50)), -5),                     # 5 keys for 10 queries
+    (dict(ck=(1, 20, 50)), -5), (dict(ck=(0, 20, 0)), -5),
+    (dict(ld=(4096, 255, 256, 4096)), -13),        # ldk below Hkv*d
+    (dict(ld=(4095, 256, 256, 4096)), -13),
+    (dict(d=80), -3), (dict(dtype=4), -2),
+    (dict(o=K + 16), -7),                          # out inside k's span
+])
+def test_attention_kv_refusals(lib, kw, status):
+    assert _call_kv(**kw) == status
+
+
+def test_attention_kv_null_key_seqlens(lib):
+    st = lib.mgattn_attention_kv(Q, K, V, O, 4096, 256, 256, 4096, (ctypes.c_int32 * 2)(0, 10), None, 1, 32, 2, 128,
+                                 0.1, 2048, 1, None)
+    assert st == -1

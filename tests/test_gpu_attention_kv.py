@@ -1,0 +1,120 @@
+"""GPU parity of mgattn_attention_kv (causal sliding-window attention with grouped
+key/value heads over a KV cache, the text decoder's attention) against the numpy f64
+oracle (oracle/gqa_window.py, pinned in tests/test_gqa_window_oracle.py), on the same
+seeded inputs, to the tolerances of the dense tests (bf16 2e-2, f32 1e-4).
+
+Shapes: the text decoder's heads (32 query heads, 2 key/value heads, head size 128,
+window 2048) in prefill longer than the window, a cache with new queries, and
+one-token decoding; plus small windows, other head groupings and head sizes, ragged
+and empty sequences, and the merged q|k|v projection layout."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle import gqa_window as G
+from tests.gpu_helpers import BF16_TOL, F32_TOL, from_device, say, to_device
+from vit_perception_encoder_amd import mgattn as mg
+from vit_perception_encoder_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+
+    assert t.cuda.is_available()
+    mg.load_library()
+    return t
+
+
+def _arr(seed, shape, dtype):
+    x = wl.normal_f32(seed, shape)
+    if dtype == wl.BF16:
+        bits = wl.f32_to_bf16_bits(x)
+        return bits, wl.bf16_bits_to_f32(bits)
+    return x, x
+
+
+def _check(torch, name, lq, lk, Hq, Hkv, d, window, dtype, seed, scale=None):
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    Tq, Tk = int(cq[-1]), int(ck[-1])
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    say(f"{name}: lq={lq} lk={lk} Hq={Hq} Hkv={Hkv} d={d} window={window} dtype={dtype}")
+    q, qf = _arr(seed, (Tq, Hq * d), dtype)
+    k, kf = _arr(seed + 1, (Tk, Hkv * d), dtype)
+    v, vf = _arr(seed + 2, (Tk, Hkv * d), dtype)
+    qd, kd, vd = (to_device(x, torch) for x in (q, k, v))
+    out = torch.full_like(qd, -777.0)
+    mg.mgattn_attention_kv(qd, kd, vd, out, Hq * d, Hkv * d, Hkv * d, Hq * d, cq, ck, len(lq), Hq, Hkv, d, scale,
+                           window, dtype, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got = from_device(out, torch).reshape(Tq, Hq, d)
+    want = G.attention_kv(qf, kf, vf, cq, ck, Hq, Hkv, d, scale, window)
+    err = np.abs(got - want)
+    tol = BF16_TOL if dtype == wl.BF16 else F32_TOL
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    assert err.max() <= tol, f"max err {err.max():.3e} at (t,h,c)={worst}"
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_text_decoder_prefill_longer_than_window(torch, dtype):
+    _check(torch, "prefill", [2600], [2600], 32, 2, 128, 2048, dtype, seed=801)
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_text_decoder_cache_with_new_queries(torch, dtype):
+    _check(torch, "cache", [300, 45], [2500, 45], 32, 2, 128, 2048, dtype, seed=811)
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_text_decoder_one_token_decode(torch, dtype):
+    lk = [1, 17, 2047, 2048, 2049, 3000]
+    _check(torch, "decode", [1] * len(lk), lk, 32, 2, 128, 2048, dtype, seed=821)
+
+
+@pytest.mark.parametrize("window", [0, 1, 2, 7, 64, 200, 257])
+def test_small_windows(torch, window):
+    _check(torch, f"window{window}", [300, 1, 77], [300, 9, 600], 4, 1, 64, window, wl.BF16, seed=831)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv", [(64, 8, 8), (96, 16, 4), (128, 6, 3), (96, 3, 1)])
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_groupings_and_head_dims(torch, d, Hq, Hkv, dtype):
+    _check(torch, "groups", [513, 0, 130], [700, 5, 130], Hq, Hkv, d, 300, dtype, seed=841)
+
+
+def test_merged_qkv_text_layout(torch):
+    """The decoder's merged projection [T, (Hq + 2*Hkv)*d]: q, k, v column views of one
+    buffer (prefill, so the cache is the same tokens)."""
+    Hq, Hkv, d, T, W = 32, 2, 128, 700, 256
+    say("merged qkv, text layout")
+    wide = (Hq + 2 * Hkv) * d
+    bits, vals = _arr(851, (T, wide), wl.BF16)
+    buf = to_device(bits, torch)
+    out = torch.empty(T, Hq * d, dtype=torch.bfloat16, device="cuda")
+    qv, kv, vv = buf[:, :Hq * d], buf[:, Hq * d:(Hq + Hkv) * d], buf[:, (Hq + Hkv) * d:]
+    mg.mgattn_attention_kv(qv, kv, vv, out, wide, wide, wide, Hq * d, [0, T], [0, T], 1, Hq, Hkv, d, 0.0883883,
+                           W, wl.BF16, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = G.attention_kv(vals[:, :Hq * d], vals[:, Hq * d:(Hq + Hkv) * d], vals[:, (Hq + Hkv) * d:], [0, T], [0, T],
+                          Hq, Hkv, d, np.float32(0.0883883), W)
+    assert np.abs(from_device(out, torch).reshape(T, Hq, d) - want).max() <= BF16_TOL
+
+
+def test_dense_path_unchanged_by_the_generalisation(torch):
+    """mgattn_attention_kv with keys = queries, Hkv = Hq and no window equals the causal
+    dense call bit for bit (one kernel serves both)."""
+    H, d, lens = 4, 96, [333, 64, 1]
+    cu = [0] + list(np.cumsum(lens))
+    T = cu[-1]
+    say("kv entry vs dense causal")
+    q, k, v = (to_device(_arr(861 + i, (T, H * d), wl.BF16)[0], torch) for i in range(3))
+    a, b = torch.empty_like(q), torch.empty_like(q)
+    s = torch.cuda.current_stream()
+    mg.mgattn_attention_kv(q, k, v, a, H * d, H * d, H * d, H * d, cu, cu, 3, H, H, d, 0.1, 0, wl.BF16, s)
+    mg.mgattn_dense(q, k, v, b, cu, 3, H, d, 0.1, 1, wl.BF16, s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

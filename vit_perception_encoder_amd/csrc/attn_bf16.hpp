@@ -65,6 +65,8 @@ struct KernelArgs {
   float c;        // |scale| * log2(e), or 1 when scale == 0 (always > 0)
   int32_t qsign;  // sign of scale: Q is multiplied by +1, -1 or 0 in registers (exact)
   int32_t ldq, ldk, ldv, ldo;  // elements between consecutive tokens of q, k, v, out
+  int32_t hq_per_kv;  // query heads per key/value head (1 without grouping)
+  int32_t window;     // causal sliding window in keys, the query's own included (0: none)
   SegTable table;
 };
 
@@ -152,14 +154,19 @@ void attn_fwd_bf16(KernelArgs a) {
 
   const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
   if (!tile.valid) return;
-  const int L = a.table.len[tile.slot];
+  const int L = a.table.len[tile.slot];    // queries of the segment
+  const int Lk = a.table.klen[tile.slot];  // keys of the segment
+  const int off = Lk - L;                  // position of query 0 among the keys
   const int q0 = tile.q0;
-  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D.
+  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D; query
+  // head h reads key/value head h / hq_per_kv.
   const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t tk0 = static_cast<size_t>(a.table.kstart[tile.slot]);
   const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const size_t kvoff = static_cast<size_t>(tile.head / a.hq_per_kv) * D;
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + t0 * a.ldq + hoff;
-  const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + t0 * a.ldk + hoff;
-  const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + t0 * a.ldv + hoff;
+  const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + tk0 * a.ldk + kvoff;
+  const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + tk0 * a.ldv + kvoff;
   __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + t0 * a.ldo + hoff;
   const int ldk = a.ldk, ldv = a.ldv;
 
@@ -174,9 +181,13 @@ void attn_fwd_bf16(KernelArgs a) {
   const int qmin = q0 + wave * 32;    // the wave's first query
 
   bf16x8 qf[KS];  // Q fragments, read from LDS once the Q tile has arrived
-  const int kend = a.causal ? min(L, q0 + BM) : L;
-  const int ntiles = (kend + BN - 1) / BN;
-  const int nsteps = (kend + SK - 1) / SK;
+  // Keys this q-tile needs: up to its last query (causal), from the first query's
+  // window start (whole tiles below it are skipped).  Tile 0 starts at key kb0.
+  const int kend = a.causal ? min(Lk, off + q0 + BM) : Lk;
+  const int kbeg = a.window > 0 ? max(0, off + q0 - a.window + 1) : 0;
+  const int kb0 = (kbeg / BN) * BN;
+  const int ntiles = (kend - kb0 + BN - 1) / BN;
+  const int nsteps = (kend - kb0 + SK - 1) / SK;
 
   // ---- LDS DMA plan.  DMA instruction i of a tile fills 64 consecutive 16-byte
   // slots (1 KB); wave w issues instructions w, w+8, ...  K slot s is row s/KSL,
@@ -199,8 +210,8 @@ void attn_fwd_bf16(KernelArgs a) {
     v_off[u] = (slot % (D / 8)) * 8;
   }
   auto issue_tile = [&](int t, int part) {  // part: 1 = K, 2 = V, 3 = both
-    const int kt0 = t * BN;
-    const int last = L - 1 - kt0;  // last valid row of this tile (>= 0)
+    const int kt0 = kb0 + t * BN;
+    const int last = Lk - 1 - kt0;  // last valid row of this tile (>= 0)
     const __bf16* kb = kg + static_cast<size_t>(kt0) * ldk;
     const __bf16* vb = vg + static_cast<size_t>(kt0) * ldv;
     __bf16* kl = lds + (t % TL::kStages) * TL::kStageElems;
@@ -284,14 +295,17 @@ void attn_fwd_bf16(KernelArgs a) {
   // (c is always positive).
   auto valu_phase = [&](int j) {
     if (j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
-    const int key0 = j * SK;
-    if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
+    const int key0 = kb0 + j * SK;
+    const int pos_lo = off + qmin;  // positions of the wave's first and last queries
+    if ((key0 + SK > Lk) || (a.causal && key0 + SK - 1 > pos_lo) ||
+        (a.window > 0 && key0 < pos_lo + 31 - a.window + 1)) {
+      const int pos = off + qr;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + b * 32 + acc_row(r, hf);
-          if (key >= L || (a.causal && key > qr)) s[b][r] = -INFINITY;
+          if (key >= Lk || (a.causal && key > pos) || (a.window > 0 && key <= pos - a.window)) s[b][r] = -INFINITY;
         }
     }
     float mx = s[0][0];
@@ -299,7 +313,10 @@ void attn_fwd_bf16(KernelArgs a) {
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
-    const float m_blk = half_swap_max(mx);
+    // a step with no key for some rows (outside their window) has maximum -inf; a
+    // finite floor keeps the reference finite (those rows get p = 0, and the first
+    // step with keys refreshes the reference with alpha = 0)
+    const float m_blk = fmaxf(half_swap_max(mx), -1.0e30f);
     if (j == 0) {
       m_run = m_blk;
     } else if (__builtin_amdgcn_ballot_w64((m_blk - m_run) * c > kRescaleLog2)) {

@@ -50,14 +50,19 @@ void attn_fwd_f32(KernelArgs a) {
 
   const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
   if (!tile.valid) return;
-  const int L = a.table.len[tile.slot];
+  const int L = a.table.len[tile.slot];    // queries of the segment
+  const int Lk = a.table.klen[tile.slot];  // keys of the segment
+  const int off = Lk - L;                  // position of query 0 among the keys
   const int q0 = tile.q0;
-  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D.
+  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D; query
+  // head h reads key/value head h / hq_per_kv.
   const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t tk0 = static_cast<size_t>(a.table.kstart[tile.slot]);
   const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const size_t kvoff = static_cast<size_t>(tile.head / a.hq_per_kv) * D;
   const float* __restrict__ qg = static_cast<const float*>(a.q) + t0 * a.ldq + hoff;
-  const float* __restrict__ kg = static_cast<const float*>(a.k) + t0 * a.ldk + hoff;
-  const float* __restrict__ vg = static_cast<const float*>(a.v) + t0 * a.ldv + hoff;
+  const float* __restrict__ kg = static_cast<const float*>(a.k) + tk0 * a.ldk + kvoff;
+  const float* __restrict__ vg = static_cast<const float*>(a.v) + tk0 * a.ldv + kvoff;
   float* __restrict__ og = static_cast<float*>(a.o) + t0 * a.ldo + hoff;
 
   const int tid = threadIdx.x;
@@ -83,18 +88,22 @@ void attn_fwd_f32(KernelArgs a) {
     for (int j = 0; j < HD; ++j) qf[j] = 0.0f;
   }
 
-  const int kend = a.causal ? min(L, q0 + BM) : L;
-  const int ntiles = (kend + BN - 1) / BN;
+  // keys this q-tile needs (causal: up to its last query; window: from its first
+  // query's window start, whole tiles below it skipped); tile 0 starts at key kb0
+  const int kend = a.causal ? min(Lk, off + q0 + BM) : Lk;
+  const int kbeg = a.window > 0 ? max(0, off + q0 - a.window + 1) : 0;
+  const int kb0 = (kbeg / BN) * BN;
+  const int ntiles = (kend - kb0 + BN - 1) / BN;
 
   f32x4 kreg[PER_T], vreg[PER_T];
   auto load_tile = [&](int t) {
-    const int kt0 = t * BN;
+    const int kt0 = kb0 + t * BN;
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int id = tid + i * NT;
       const int key = id / (D / 4), part = id % (D / 4);
       const int row = kt0 + key;
-      const bool in = row < L;
+      const bool in = row < Lk;
       kreg[i] = in ? *reinterpret_cast<const f32x4*>(kg + static_cast<size_t>(row) * a.ldk + part * 4) : f32x4{};
       vreg[i] = in ? *reinterpret_cast<const f32x4*>(vg + static_cast<size_t>(row) * a.ldv + part * 4) : f32x4{};
     }
@@ -125,7 +134,7 @@ void attn_fwd_f32(KernelArgs a) {
     if (t + 1 < ntiles) load_tile(t + 1);
     const float* ks = lds + buf * TL::kStageElems;
     const float* vs = ks + TL::kTileElems;
-    const int kt0 = t * BN;
+    const int kt0 = kb0 + t * BN;
 
     f32x16 s = f32x16{};
 #pragma unroll
@@ -135,19 +144,23 @@ void attn_fwd_f32(KernelArgs a) {
       for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[e], qf[4 * j + e], s, 0, 0, 0);
     }
 
-    const bool masked = (kt0 + BN > L) || (a.causal && kt0 + BN - 1 > q0 + wave * 32);
+    const int pos_lo = off + q0 + wave * 32;  // position of the wave's first query
+    const int pos = off + qr;
+    const bool masked = (kt0 + BN > Lk) || (a.causal && kt0 + BN - 1 > pos_lo) ||
+                        (a.window > 0 && kt0 < pos_lo + 31 - a.window + 1);
+    auto is_masked = [&](int key) {
+      return key >= Lk || (a.causal && key > pos) || (a.window > 0 && key <= pos - a.window);
+    };
     if (masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt0 + acc_row(r, hf);
-        if (key >= L || (a.causal && key > qr)) s[r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (is_masked(kt0 + acc_row(r, hf))) s[r] = -INFINITY;
     }
 
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    const float m_tile = half_swap_max(mx);
+    const float m_tile = fmaxf(half_swap_max(mx), -1.0e30f);  // finite for rows without keys here
     if (t == 0) {
       m_run = m_tile;
     } else if (__builtin_amdgcn_ballot_w64((m_tile - m_run) * c > kRescaleLog2)) {
@@ -164,10 +177,7 @@ void attn_fwd_f32(KernelArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mc));
-      if (masked) {
-        const int key = kt0 + acc_row(r, hf);
-        if (key >= L || (a.causal && key > qr)) p = 0.0f;
-      }
+      if (masked && is_masked(kt0 + acc_row(r, hf))) p = 0.0f;
       s[r] = p;
       lsum += p;
     }

@@ -66,41 +66,63 @@ size_t span_bytes(int64_t T, int64_t ld, int H, int d, int dtype) {
   return (static_cast<size_t>(T - 1) * static_cast<size_t>(ld) + static_cast<size_t>(H) * d) * elem_size(dtype);
 }
 
+// Prefix-sum array of n+1 entries: starts at 0, non-decreasing, total > 0.  Writes the
+// total and the longest entry.
+int check_seqlens(const int32_t* cu, int n, int64_t* total, int64_t* longest) {
+  if (cu[0] != 0) return MGATTN_ERR_SEQLENS;
+  int64_t m = 0;
+  for (int g = 0; g < n; ++g) {
+    if (cu[g + 1] < cu[g]) return MGATTN_ERR_SEQLENS;
+    m = std::max<int64_t>(m, static_cast<int64_t>(cu[g + 1]) - cu[g]);
+  }
+  if (cu[n] <= 0) return MGATTN_ERR_SEQLENS;
+  *total = cu[n];
+  *longest = m;
+  return MGATTN_OK;
+}
+
 // Checks every argument that needs no GPU.  ld* are the leading dimensions
-// (elements between consecutive tokens).  On success, *T_out is the token count.
+// (elements between consecutive tokens).  Keys and values have Hkv heads and, when
+// cuk is not NULL, their own segments (cuk[g+1] - cuk[g] >= cu[g+1] - cu[g]).
 int validate(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
-             int64_t ldo, const int32_t* cu, int n_seg, int H, int d, float scale, int causal, int dtype,
-             int64_t* T_out) {
+             int64_t ldo, const int32_t* cu, const int32_t* cuk, int n_seg, int H, int Hkv, int d, float scale,
+             int causal, int window, int dtype) {
   if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
   if (!q || !k || !v || !out || !cu) return MGATTN_ERR_NULL;
   if (n_seg < 1) return MGATTN_ERR_SEGMENTS;
-  if (H < 1) return MGATTN_ERR_HEADS;
+  if (H < 1 || Hkv < 1 || H % Hkv != 0) return MGATTN_ERR_HEADS;
   if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
   if (!isfinite(scale) || (causal != 0 && causal != 1)) return MGATTN_ERR_SCALE;
-  const int64_t row = static_cast<int64_t>(H) * d;
+  if (window < 0) return MGATTN_ERR_WINDOW;
+  const int64_t row_q = static_cast<int64_t>(H) * d, row_kv = static_cast<int64_t>(Hkv) * d;
   const int64_t align_elems = 16 / static_cast<int64_t>(elem_size(dtype));
-  for (int64_t ld : {ldq, ldk, ldv, ldo})
-    if (ld < row || ld > INT32_MAX || ld % align_elems != 0) return MGATTN_ERR_STRIDE;
-  if (cu[0] != 0) return MGATTN_ERR_SEQLENS;
-  int64_t max_len = 0;
-  for (int g = 0; g < n_seg; ++g) {
-    if (cu[g + 1] < cu[g]) return MGATTN_ERR_SEQLENS;
-    const int64_t len = static_cast<int64_t>(cu[g + 1]) - cu[g];
-    if (len > max_len) max_len = len;
+  for (int64_t ld : {ldq, ldo})
+    if (ld < row_q || ld > INT32_MAX || ld % align_elems != 0) return MGATTN_ERR_STRIDE;
+  for (int64_t ld : {ldk, ldv})
+    if (ld < row_kv || ld > INT32_MAX || ld % align_elems != 0) return MGATTN_ERR_STRIDE;
+  int64_t Tq = 0, Tk = 0, max_q = 0, max_k = 0;
+  int st = check_seqlens(cu, n_seg, &Tq, &max_q);
+  if (st != MGATTN_OK) return st;
+  if (cuk) {
+    st = check_seqlens(cuk, n_seg, &Tk, &max_k);
+    if (st != MGATTN_OK) return st;
+    for (int g = 0; g < n_seg; ++g)
+      if (cuk[g + 1] - cuk[g] < cu[g + 1] - cu[g]) return MGATTN_ERR_SEQLENS;
+  } else {
+    Tk = Tq;
+    max_k = max_q;
   }
-  const int64_t T = cu[n_seg];
-  if (T <= 0) return MGATTN_ERR_SEQLENS;
   // the workgroup's element offsets inside one segment stay below 2^31 bytes
-  const int64_t ld_max = std::max(std::max(ldq, ldk), std::max(ldv, ldo));
-  if (max_len * ld_max * static_cast<int64_t>(elem_size(dtype)) > INT32_MAX) return MGATTN_ERR_SIZE;
+  const int64_t es = static_cast<int64_t>(elem_size(dtype));
+  if (max_q * std::max(ldq, ldo) * es > INT32_MAX || max_k * std::max(ldk, ldv) * es > INT32_MAX)
+    return MGATTN_ERR_SIZE;
   if (((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
         reinterpret_cast<uintptr_t>(out)) & 15u) != 0)
     return MGATTN_ERR_ALIGN;
-  const size_t bo = span_bytes(T, ldo, H, d, dtype);
-  if (overlaps(out, bo, q, span_bytes(T, ldq, H, d, dtype)) || overlaps(out, bo, k, span_bytes(T, ldk, H, d, dtype)) ||
-      overlaps(out, bo, v, span_bytes(T, ldv, H, d, dtype)))
+  const size_t bo = span_bytes(Tq, ldo, H, d, dtype);
+  if (overlaps(out, bo, q, span_bytes(Tq, ldq, H, d, dtype)) || overlaps(out, bo, k, span_bytes(Tk, ldk, Hkv, d, dtype)) ||
+      overlaps(out, bo, v, span_bytes(Tk, ldv, Hkv, d, dtype)))
     return MGATTN_ERR_ALIAS;
-  *T_out = T;
   return MGATTN_OK;
 }
 
@@ -161,14 +183,18 @@ int blocks_for(int64_t items, unsigned* grid) {
 
 extern "C" {
 
-int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk,
-                         int64_t ldv, int64_t ldo, const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
-                         int causal, int dtype, void* stream) {
-  int64_t T = 0;
-  const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens, n_seg, H, d, scale, causal, dtype, &T);
+}  // extern "C"
+
+namespace {
+
+// Validation, plan and launches shared by every attention entry point.
+int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
+           int64_t ldo, const int32_t* cu, const int32_t* cuk, int n_seg, int H, int Hkv, int d, float scale,
+           int causal, int window, int dtype, void* stream) {
+  const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu, cuk, n_seg, H, Hkv, d, scale, causal, window, dtype);
   if (st != MGATTN_OK) return st;
   std::vector<Launch> plan;
-  if (!make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
+  if (!make_plan(cu, cuk, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
   if (!device_ok()) return MGATTN_ERR_DEVICE;
 
   KernelArgs args;
@@ -183,6 +209,8 @@ int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out,
   args.ldk = static_cast<int32_t>(ldk);
   args.ldv = static_cast<int32_t>(ldv);
   args.ldo = static_cast<int32_t>(ldo);
+  args.hq_per_kv = H / Hkv;
+  args.window = window;
   // c = |scale| * log2(e) multiplies the scores inside exp2; the sign of scale goes
   // into Q (exact).  For scale == 0 the scores vanish (Q * 0) and c = 1 keeps masked
   // keys at exp2(-inf) = 0.
@@ -205,6 +233,25 @@ int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out,
   return MGATTN_ERR_HEAD_DIM;
 }
 
+}  // namespace
+
+extern "C" {
+
+int mgattn_dense_strided(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk,
+                         int64_t ldv, int64_t ldo, const int32_t* cu_seqlens, int n_seg, int H, int d, float scale,
+                         int causal, int dtype, void* stream) {
+  return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens, nullptr, n_seg, H, H, d, scale, causal, 0, dtype,
+                stream);
+}
+
+int mgattn_attention_kv(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk,
+                        int64_t ldv, int64_t ldo, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int n_seq, int Hq, int Hkv, int d, float scale, int window, int dtype, void* stream) {
+  if (!cu_seqlens_k) return MGATTN_ERR_NULL;
+  return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1, window,
+                dtype, stream);
+}
+
 int mgattn_dense(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,
                  int n_seg, int H, int d, float scale, int causal, int dtype, void* stream) {
   const int64_t row = static_cast<int64_t>(H) * d;
@@ -218,7 +265,7 @@ const char* mgattn_strerror(int status) {
     case MGATTN_ERR_NULL: return "a required pointer (q, k, v, out or cu_seqlens) is NULL";
     case MGATTN_ERR_DTYPE: return "dtype is not MGATTN_F32 or MGATTN_BF16";
     case MGATTN_ERR_HEAD_DIM: return "head_dim not supported (supported: 64, 96, 128)";
-    case MGATTN_ERR_HEADS: return "H must be >= 1";
+    case MGATTN_ERR_HEADS: return "heads must be >= 1 (and Hq a multiple of Hkv)";
     case MGATTN_ERR_SEQLENS:
       return "cu_seqlens must start at 0, be non-decreasing and end at T > 0";
     case MGATTN_ERR_SEGMENTS: return "n_seg must be >= 1";
@@ -228,6 +275,7 @@ const char* mgattn_strerror(int status) {
     case MGATTN_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
     case MGATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case MGATTN_ERR_SIZE: return "a segment spans more than 2^31 bytes, or the grid is too large";
+    case MGATTN_ERR_WINDOW: return "window must be >= 0";
     case MGATTN_ERR_GRID:
       return "a patch grid is empty, more than 64 images, a window below 1, or inverse not 0 or 1";
     case MGATTN_ERR_STRIDE:
@@ -264,7 +312,7 @@ int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
     if (cu_seqlens[g + 1] < cu_seqlens[g]) return MGATTN_ERR_SEQLENS;
   if (cu_seqlens[n_seg] <= 0) return MGATTN_ERR_SEQLENS;
   std::vector<Launch> plan;
-  if (!make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
+  if (!make_plan(cu_seqlens, nullptr, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
   for (int i = 0; i < static_cast<int>(plan.size()) && i < max_launches; ++i)
     if (grids) grids[i] = plan[i].grid;
   return static_cast<int>(plan.size());
@@ -276,7 +324,7 @@ int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
   const int nl = mgattn_dense_plan(cu_seqlens, n_seg, H, d, dtype, causal, nullptr, 0);
   if (nl < 0) return nl;
   std::vector<Launch> plan;
-  make_plan(cu_seqlens, n_seg, H, block_m_of(d, dtype), plan);
+  make_plan(cu_seqlens, nullptr, n_seg, H, block_m_of(d, dtype), plan);
   if (launch < 0 || launch >= nl || block < 0 || block >= plan[launch].grid) return MGATTN_ERR_SIZE;
   const Tile t = decode_tile(plan[launch].table, H, block_m_of(d, dtype), causal, static_cast<int>(block));
   if (!t.valid) return 0;

@@ -29,8 +29,10 @@ constexpr int kXcds = 8;
 struct SegTable {
   int32_t n;                                // segments in this launch
   int32_t nx;                               // XCD groups: 8 if H % 8 == 0, else 1
-  int32_t start[kMaxSegPerLaunch];          // first token of each segment
-  int32_t len[kMaxSegPerLaunch];            // tokens in each segment (> 0)
+  int32_t start[kMaxSegPerLaunch];          // first query token of each segment
+  int32_t len[kMaxSegPerLaunch];            // queries in each segment (> 0)
+  int32_t kstart[kMaxSegPerLaunch];         // first key token (= start without a KV cache)
+  int32_t klen[kMaxSegPerLaunch];           // keys (>= len; = len without a KV cache)
   int32_t tile_prefix[kMaxSegPerLaunch + 1];  // exclusive prefix of ceil(len / block_m)
 };
 
@@ -75,15 +77,20 @@ struct Launch {
   int64_t grid;
 };
 
-// Builds the launches for already-validated arguments.  Returns false if a launch
-// would need more workgroups than a grid dimension holds.
-inline bool make_plan(const int32_t* cu, int n_seg, int H, int block_m, std::vector<Launch>& out) {
-  struct Seg { int32_t start, len; int orig; };
+// Builds the launches for already-validated arguments.  cuk (may be NULL: keys are
+// the queries) gives each segment's key rows when queries attend a longer key range
+// (a KV cache).  Returns false if a launch would need more workgroups than a grid
+// dimension holds.
+inline bool make_plan(const int32_t* cu, const int32_t* cuk, int n_seg, int H, int block_m,
+                      std::vector<Launch>& out) {
+  struct Seg { int32_t start, len, kstart, klen; int orig; };
   std::vector<Seg> segs;
   segs.reserve(n_seg);
   for (int g = 0; g < n_seg; ++g) {
     const int32_t len = cu[g + 1] - cu[g];
-    if (len > 0) segs.push_back({cu[g], len, g});
+    const int32_t ks = cuk ? cuk[g] : cu[g];
+    const int32_t kl = cuk ? cuk[g + 1] - cuk[g] : len;
+    if (len > 0) segs.push_back({cu[g], len, ks, kl, g});
   }
   std::stable_sort(segs.begin(), segs.end(), [](const Seg& a, const Seg& b) { return a.len > b.len; });
   out.clear();
@@ -100,6 +107,8 @@ inline bool make_plan(const int32_t* cu, int n_seg, int H, int block_m, std::vec
       const Seg& s = segs[s0 + j];
       l.table.start[j] = s.start;
       l.table.len[j] = s.len;
+      l.table.kstart[j] = s.kstart;
+      l.table.klen[j] = s.klen;
       tiles += (s.len + block_m - 1) / block_m;
       if (tiles * H > std::numeric_limits<int32_t>::max()) return false;
       l.table.tile_prefix[j + 1] = static_cast<int32_t>(tiles);

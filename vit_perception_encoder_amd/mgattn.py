@@ -23,10 +23,10 @@ STATUS_NAMES = {
     -4: "MGATTN_ERR_HEADS", -5: "MGATTN_ERR_SEQLENS", -6: "MGATTN_ERR_SEGMENTS",
     -7: "MGATTN_ERR_ALIAS", -8: "MGATTN_ERR_ALIGN", -9: "MGATTN_ERR_SCALE",
     -10: "MGATTN_ERR_LAUNCH", -11: "MGATTN_ERR_DEVICE", -12: "MGATTN_ERR_SIZE", -13: "MGATTN_ERR_STRIDE",
-    -14: "MGATTN_ERR_GRID",
+    -14: "MGATTN_ERR_GRID", -15: "MGATTN_ERR_WINDOW",
 }
 
-EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
+EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_attention_kv", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
            "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
            "mgattn_window_permute", "mgattn_rope2d", "mgattn_version"]
 
@@ -55,6 +55,9 @@ def load_library(path: str | os.PathLike | None = None):
     lib.mgattn_dense.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, i32, vp]
     lib.mgattn_dense_strided.restype = i32
     lib.mgattn_dense_strided.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, i32, i32, f32, i32, i32, vp]
+    lib.mgattn_attention_kv.restype = i32
+    lib.mgattn_attention_kv.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i32, i32, i32, i32, f32, i32,
+                                        i32, vp]
     lib.mgattn_strerror.restype = ctypes.c_char_p
     lib.mgattn_strerror.argtypes = [i32]
     lib.mgattn_dense_supported.restype = i32
@@ -132,6 +135,24 @@ def mgattn_dense_strided(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, c
                                   int(causal), int(dtype), _stream(stream))
     if check and st != 0:
         raise MgattnError(st, "mgattn_dense_strided")
+    return st
+
+
+def mgattn_attention_kv(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu_seqlens_q: Sequence[int],
+                        cu_seqlens_k: Sequence[int], n_seq: int, Hq: int, Hkv: int, d: int, scale: float,
+                        window: int, dtype: int, stream=None, check: bool = True) -> int:
+    """Causal sliding-window GQA attention over a key/value cache (see
+    mgattn_attention_kv in include/mgattn.h)."""
+    lib = load_library()
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_k)
+    if nq < n_seq + 1 or nk < n_seq + 1:
+        raise ValueError(f"cu_seqlens_q/k need {n_seq + 1} entries")
+    st = lib.mgattn_attention_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
+                                 ctypes.cast(cq, ctypes.c_void_p), ctypes.cast(ck, ctypes.c_void_p), int(n_seq),
+                                 int(Hq), int(Hkv), int(d), float(scale), int(window), int(dtype), _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_attention_kv")
     return st
 
 
