@@ -39,7 +39,7 @@ METRIC = "attention TFLOP/s (%bf16 MFMA peak) + ms per 50-layer tower attn @4096
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published 2.5 PFLOP/s): 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published 8 TB/s)
 THETA = 10000.0
-KERNEL_NAME = "attn_fwd_bf16<96>"
+KERNEL_NAME = "attn_fwd_bf16<96, false>"  # the dense instantiation
 TRAFFIC_FILE = ROOT / "profiles" / "attn_fwd_bf16_96_tower4096_traffic.json"
 KERNEL_SOURCES = ["vit_perception_encoder_amd/csrc/attn_bf16.hpp", "vit_perception_encoder_amd/csrc/plan.hpp",
                   "vit_perception_encoder_amd/csrc/mgattn.hip"]

@@ -133,7 +133,11 @@ __device__ inline bf16x4 ds_read_tr(const __bf16* p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int D>
+// kGeneral: keys from their own segment rows (a KV cache), grouped key/value heads and
+// a sliding window are read from the arguments.  Without it (the dense entry points)
+// keys are the queries, heads are not grouped and there is no window, as compile-time
+// facts, so the dense kernel carries none of that arithmetic.
+template <int D, bool kGeneral>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(KernelArgs a) {
   using TL = Bf16Tile<D>;
@@ -154,16 +158,17 @@ void attn_fwd_bf16(KernelArgs a) {
 
   const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
   if (!tile.valid) return;
-  const int L = a.table.len[tile.slot];    // queries of the segment
-  const int Lk = a.table.klen[tile.slot];  // keys of the segment
-  const int off = Lk - L;                  // position of query 0 among the keys
+  const int L = a.table.len[tile.slot];                   // queries of the segment
+  const int Lk = kGeneral ? a.table.klen[tile.slot] : L;  // keys of the segment
+  const int off = Lk - L;                                 // position of query 0 among the keys
+  const int window = kGeneral ? a.window : 0;
   const int q0 = tile.q0;
   // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D; query
   // head h reads key/value head h / hq_per_kv.
   const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
-  const size_t tk0 = static_cast<size_t>(a.table.kstart[tile.slot]);
+  const size_t tk0 = kGeneral ? static_cast<size_t>(a.table.kstart[tile.slot]) : t0;
   const size_t hoff = static_cast<size_t>(tile.head) * D;
-  const size_t kvoff = static_cast<size_t>(tile.head / a.hq_per_kv) * D;
+  const size_t kvoff = kGeneral ? static_cast<size_t>(tile.head / a.hq_per_kv) * D : hoff;
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + t0 * a.ldq + hoff;
   const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + tk0 * a.ldk + kvoff;
   const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + tk0 * a.ldv + kvoff;
@@ -184,7 +189,7 @@ void attn_fwd_bf16(KernelArgs a) {
   // Keys this q-tile needs: up to its last query (causal), from the first query's
   // window start (whole tiles below it are skipped).  Tile 0 starts at key kb0.
   const int kend = a.causal ? min(Lk, off + q0 + BM) : Lk;
-  const int kbeg = a.window > 0 ? max(0, off + q0 - a.window + 1) : 0;
+  const int kbeg = window > 0 ? max(0, off + q0 - window + 1) : 0;
   const int kb0 = (kbeg / BN) * BN;
   const int ntiles = (kend - kb0 + BN - 1) / BN;
   const int nsteps = (kend - kb0 + SK - 1) / SK;
@@ -298,14 +303,14 @@ void attn_fwd_bf16(KernelArgs a) {
     const int key0 = kb0 + j * SK;
     const int pos_lo = off + qmin;  // positions of the wave's first and last queries
     if ((key0 + SK > Lk) || (a.causal && key0 + SK - 1 > pos_lo) ||
-        (a.window > 0 && key0 < pos_lo + 31 - a.window + 1)) {
+        (window > 0 && key0 < pos_lo + 31 - window + 1)) {
       const int pos = off + qr;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + b * 32 + acc_row(r, hf);
-          if (key >= Lk || (a.causal && key > pos) || (a.window > 0 && key <= pos - a.window)) s[b][r] = -INFINITY;
+          if (key >= Lk || (a.causal && key > pos) || (window > 0 && key <= pos - window)) s[b][r] = -INFINITY;
         }
     }
     float mx = s[0][0];

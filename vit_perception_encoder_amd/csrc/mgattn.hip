@@ -217,11 +217,18 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   args.c = scale == 0.0f ? 1.0f : static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);
   args.qsign = scale > 0.0f ? 1 : (scale < 0.0f ? -1 : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool general = cuk != nullptr || Hkv != H || window != 0;
   if (dtype == MGATTN_BF16) {
     switch (d) {
-      case 64: return launch_all(attn_fwd_bf16<64>, Bf16Tile<64>::kThreads, plan, args, s);
-      case 96: return launch_all(attn_fwd_bf16<96>, Bf16Tile<96>::kThreads, plan, args, s);
-      case 128: return launch_all(attn_fwd_bf16<128>, Bf16Tile<128>::kThreads, plan, args, s);
+      case 64:
+        return general ? launch_all(attn_fwd_bf16<64, true>, Bf16Tile<64>::kThreads, plan, args, s)
+                       : launch_all(attn_fwd_bf16<64, false>, Bf16Tile<64>::kThreads, plan, args, s);
+      case 96:
+        return general ? launch_all(attn_fwd_bf16<96, true>, Bf16Tile<96>::kThreads, plan, args, s)
+                       : launch_all(attn_fwd_bf16<96, false>, Bf16Tile<96>::kThreads, plan, args, s);
+      case 128:
+        return general ? launch_all(attn_fwd_bf16<128, true>, Bf16Tile<128>::kThreads, plan, args, s)
+                       : launch_all(attn_fwd_bf16<128, false>, Bf16Tile<128>::kThreads, plan, args, s);
     }
   } else {
     switch (d) {
