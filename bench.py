@@ -143,6 +143,32 @@ def token_path(torch, mg, wl, layers):
                                         "frac_hbm": moved / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS}
         res[f"rope2d_qk_{name}"] = {"ms": ms_r, "launches": 2, "bytes": rot, "gbs": rot / (ms_r * 1e-3) / 1e9,
                                     "frac_hbm": rot / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    # text decoder attention (32 query / 2 key-value heads, head size 128, window 2048)
+    Hq, Hkv, dt, W = 32, 2, 128, 2048
+    L = 8192
+    q = torch.randn(L, Hq * dt, device=dev).to(torch.bfloat16)
+    k = torch.randn(L, Hkv * dt, device=dev).to(torch.bfloat16)
+    v = torch.randn(L, Hkv * dt, device=dev).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    ms = time_launches(torch, lambda: mg.mgattn_attention_kv(q, k, v, o, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt, [0, L],
+                                                            [0, L], 1, Hq, Hkv, dt, dt ** -0.5, W, mg.MGATTN_BF16,
+                                                            stream))
+    visible = sum(min(i + 1, W) for i in range(L))
+    fl = 4.0 * dt * Hq * visible
+    res["text_prefill_8192_window2048"] = {"ms": ms, "gflop": fl / 1e9, "tflops": fl / (ms * 1e-3) / 1e12,
+                                           "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    B, Lk = 32, 4096
+    qd = torch.randn(B, Hq * dt, device=dev).to(torch.bfloat16)
+    kc = torch.randn(B * Lk, Hkv * dt, device=dev).to(torch.bfloat16)
+    vc = torch.randn(B * Lk, Hkv * dt, device=dev).to(torch.bfloat16)
+    od = torch.empty_like(qd)
+    cq = list(range(B + 1))
+    ck = [i * Lk for i in range(B + 1)]
+    ms = time_launches(torch, lambda: mg.mgattn_attention_kv(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt, cq,
+                                                            ck, B, Hq, Hkv, dt, dt ** -0.5, W, mg.MGATTN_BF16, stream))
+    kv_bytes = B * min(Lk, W) * Hkv * dt * 2 * 2  # the window's K and V, read once
+    res["text_decode_32x4096_window2048"] = {"ms": ms, "kv_bytes": kv_bytes, "gbs": kv_bytes / (ms * 1e-3) / 1e9,
+                                             "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return res
 
 
@@ -253,7 +279,8 @@ def main() -> int:
     full_tf = layers[full_idx[0]][5] / (full_ms * 1e-3) / 1e12
     win_tf = layers[win_idx[0]][5] / (win_ms * 1e-3) / 1e12
 
-    print("[bench] timing the other entry points (merged qkv, window gather, 2D RoPE)", file=sys.stderr, flush=True)
+    print("[bench] timing the other entry points (merged qkv, window gather, 2D RoPE, text decoder)", file=sys.stderr,
+          flush=True)
     token = token_path(torch, mg, wl, layers)
 
     if args.copy_calibration:

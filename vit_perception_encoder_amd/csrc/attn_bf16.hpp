@@ -153,26 +153,38 @@ void attn_fwd_bf16(KernelArgs a) {
   constexpr int VDMA_W = (VDMA + TL::kWaves - 1) / TL::kWaves;
   constexpr float kRescaleLog2 = 8.0f;  // refresh the running max past 2^8 growth
   static_assert(TL::kQBlocks == 1, "one 32-query block per wave");
+  // K operands of the next QK product are read during the softmax phase, except in the
+  // general head_dim-128 instantiation, where their 64 registers would spill: there
+  // they are read in the MFMA phase that uses them (the tile is resident by then).
+  constexpr bool kPrefetchK = !(kGeneral && D >= 128);
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
 
   const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
   if (!tile.valid) return;
-  const int L = a.table.len[tile.slot];                   // queries of the segment
+  // Query rows.  The general instantiation packs the G query heads that share a
+  // key/value head into the rows of one tile (row r = token r / G, query head
+  // kvhead * G + r % G), so K and V are read once per key/value head; the dense one
+  // has G = 1 and the tile's own head.
+  const int G = kGeneral ? a.hq_per_kv : 1;
+  const int L = a.table.len[tile.slot];                   // query tokens of the segment
+  const int R = L * G;                                    // query rows
   const int Lk = kGeneral ? a.table.klen[tile.slot] : L;  // keys of the segment
-  const int off = Lk - L;                                 // position of query 0 among the keys
+  const int off = Lk - L;                                 // position of query token 0 among the keys
   const int window = kGeneral ? a.window : 0;
-  const int q0 = tile.q0;
-  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D; query
-  // head h reads key/value head h / hq_per_kv.
+  const int q0 = tile.q0;                                 // first row of the tile
+  // Token t, head h of a tensor with leading dimension ld starts at t*ld + h*D.
   const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
   const size_t tk0 = kGeneral ? static_cast<size_t>(a.table.kstart[tile.slot]) : t0;
-  const size_t hoff = static_cast<size_t>(tile.head) * D;
-  const size_t kvoff = kGeneral ? static_cast<size_t>(tile.head / a.hq_per_kv) * D : hoff;
-  const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + t0 * a.ldq + hoff;
+  const size_t kvoff = static_cast<size_t>(tile.head) * D;  // key/value head (= the query head when G = 1)
+  auto row_offset = [&](int r, int ld) {  // offset of query row r in q or out
+    const int qh = kGeneral ? tile.head * G + r % G : tile.head;
+    return static_cast<size_t>(r / G) * ld + static_cast<size_t>(qh) * D;
+  };
+  const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + t0 * a.ldq;
   const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + tk0 * a.ldk + kvoff;
   const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + tk0 * a.ldv + kvoff;
-  __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + t0 * a.ldo + hoff;
+  __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + t0 * a.ldo;
   const int ldk = a.ldk, ldv = a.ldv;
 
   const int tid = threadIdx.x;
@@ -182,14 +194,16 @@ void attn_fwd_bf16(KernelArgs a) {
   const int n = lane & 31;
   const int hf = lane >> 5;
   const float c = a.c;
-  const int qr = q0 + wave * 32 + n;  // this lane's query (relative to the segment)
-  const int qmin = q0 + wave * 32;    // the wave's first query
+  const int qr = q0 + wave * 32 + n;  // this lane's query row (relative to the segment)
+  const int qmin = q0 + wave * 32;    // the wave's first row
+  const int qpos = off + qr / G;      // the lane's query position among the keys
 
   bf16x8 qf[KS];  // Q fragments, read from LDS once the Q tile has arrived
-  // Keys this q-tile needs: up to its last query (causal), from the first query's
-  // window start (whole tiles below it are skipped).  Tile 0 starts at key kb0.
-  const int kend = a.causal ? min(Lk, off + q0 + BM) : Lk;
-  const int kbeg = window > 0 ? max(0, off + q0 - window + 1) : 0;
+  // Keys this q-tile needs: up to its last query token (causal), from its first
+  // token's window start (whole tiles below it are skipped).  Tile 0 starts at kb0.
+  const int tok_last = (min(R, q0 + BM) - 1) / G;
+  const int kend = a.causal ? min(Lk, off + tok_last + 1) : Lk;
+  const int kbeg = window > 0 ? max(0, off + q0 / G - window + 1) : 0;
   const int kb0 = (kbeg / BN) * BN;
   const int ntiles = (kend - kb0 + BN - 1) / BN;
   const int nsteps = (kend - kb0 + SK - 1) / SK;
@@ -299,12 +313,11 @@ void attn_fwd_bf16(KernelArgs a) {
   // past the segment end and (causal) keys after the query get s = -inf, hence p = 0
   // (c is always positive).
   auto valu_phase = [&](int j) {
-    if (j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
+    if (kPrefetchK && j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
     const int key0 = kb0 + j * SK;
-    const int pos_lo = off + qmin;  // positions of the wave's first and last queries
-    if ((key0 + SK > Lk) || (a.causal && key0 + SK - 1 > pos_lo) ||
-        (window > 0 && key0 < pos_lo + 31 - window + 1)) {
-      const int pos = off + qr;
+    const int pos_lo = off + qmin / G, pos_hi = off + (qmin + 31) / G;  // the wave's first and last positions
+    if ((key0 + SK > Lk) || (a.causal && key0 + SK - 1 > pos_lo) || (window > 0 && key0 < pos_hi - window + 1)) {
+      const int pos = qpos;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -371,7 +384,7 @@ void attn_fwd_bf16(KernelArgs a) {
   for (int u = 0; u < QDMA / TL::kWaves; ++u) {
     const int i = wave + TL::kWaves * u;
     const int slot = i * 64 + lane;
-    dma16(qg + static_cast<size_t>(min(q0 + slot / (D / 8), L - 1)) * a.ldq + (slot % (D / 8)) * 8,
+    dma16(qg + row_offset(min(q0 + slot / (D / 8), R - 1), a.ldq) + (slot % (D / 8)) * 8,
           __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
   }
   while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++, 3);
@@ -386,7 +399,7 @@ void attn_fwd_bf16(KernelArgs a) {
 #pragma unroll
   for (int s = 0; s < KS; ++s)
     qf[s] = *reinterpret_cast<const bf16x8*>(ql + (wave * 32 + n) * D + 16 * s + 8 * hf);
-  if (qr >= L) {
+  if (qr >= R) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
   }
@@ -436,6 +449,7 @@ void attn_fwd_bf16(KernelArgs a) {
       stage_end(2 * j + 1);
       __syncthreads();
       stage_begin(2 * j + 2);
+      if (!kPrefetchK) read_k(j + 1);
       mfma_qk();
       mfma_pv(j);
       stage_end(2 * j + 2);
@@ -467,6 +481,7 @@ void attn_fwd_bf16(KernelArgs a) {
       stage_end(2 * j + 2);
       __syncthreads();
       stage_begin(2 * j + 3);
+      if (!kPrefetchK) read_k(j + 1);
       mfma_qk();
       mfma_pv(j);
       stage_end(2 * j + 3);
@@ -513,8 +528,8 @@ void attn_fwd_bf16(KernelArgs a) {
   for (int u = 0; u < NU; ++u) {
     const int cidx = u * 64 + lane;
     const int row = cidx / CH;
-    if (qmin + row < L)
-      *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(qmin + row) * a.ldo + (cidx % CH) * 8) = piece_val[u];
+    if (qmin + row < R)
+      *reinterpret_cast<bf16x8*>(og + row_offset(qmin + row, a.ldo) + (cidx % CH) * 8) = piece_val[u];
   }
 }
 

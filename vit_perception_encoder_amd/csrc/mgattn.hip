@@ -112,6 +112,7 @@ int validate(const void* q, const void* k, const void* v, void* out, int64_t ldq
     Tk = Tq;
     max_k = max_q;
   }
+  if (max_q * (H / Hkv) > INT32_MAX) return MGATTN_ERR_SIZE;  // packed query rows of a segment
   // the workgroup's element offsets inside one segment stay below 2^31 bytes
   const int64_t es = static_cast<int64_t>(elem_size(dtype));
   if (max_q * std::max(ldq, ldo) * es > INT32_MAX || max_k * std::max(ldk, ldv) * es > INT32_MAX)
@@ -193,8 +194,13 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
            int causal, int window, int dtype, void* stream) {
   const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu, cuk, n_seg, H, Hkv, d, scale, causal, window, dtype);
   if (st != MGATTN_OK) return st;
+  // The general bf16 kernel packs the query heads of a key/value head into one tile's
+  // rows: its tiles are per key/value head, H/Hkv rows per token.
+  const bool general = cuk != nullptr || Hkv != H || window != 0;
+  const bool pack = general && dtype == MGATTN_BF16;
+  const int H_tiles = pack ? Hkv : H;
   std::vector<Launch> plan;
-  if (!make_plan(cu, cuk, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
+  if (!make_plan(cu, cuk, n_seg, H_tiles, block_m_of(d, dtype), plan, pack ? H / Hkv : 1)) return MGATTN_ERR_SIZE;
   if (!device_ok()) return MGATTN_ERR_DEVICE;
 
   KernelArgs args;
@@ -203,7 +209,7 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   args.k = k;
   args.v = v;
   args.o = out;
-  args.H = H;
+  args.H = H_tiles;
   args.causal = causal;
   args.ldq = static_cast<int32_t>(ldq);
   args.ldk = static_cast<int32_t>(ldk);
@@ -217,7 +223,6 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   args.c = scale == 0.0f ? 1.0f : static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);
   args.qsign = scale > 0.0f ? 1 : (scale < 0.0f ? -1 : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool general = cuk != nullptr || Hkv != H || window != 0;
   if (dtype == MGATTN_BF16) {
     switch (d) {
       case 64:

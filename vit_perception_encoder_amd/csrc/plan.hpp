@@ -33,7 +33,7 @@ struct SegTable {
   int32_t len[kMaxSegPerLaunch];            // queries in each segment (> 0)
   int32_t kstart[kMaxSegPerLaunch];         // first key token (= start without a KV cache)
   int32_t klen[kMaxSegPerLaunch];           // keys (>= len; = len without a KV cache)
-  int32_t tile_prefix[kMaxSegPerLaunch + 1];  // exclusive prefix of ceil(len / block_m)
+  int32_t tile_prefix[kMaxSegPerLaunch + 1];  // exclusive prefix of ceil(len * rows_per_token / block_m)
 };
 
 struct Tile {
@@ -81,8 +81,10 @@ struct Launch {
 // the queries) gives each segment's key rows when queries attend a longer key range
 // (a KV cache).  Returns false if a launch would need more workgroups than a grid
 // dimension holds.
+// rows_per_token: query rows of a token in one tile (the query heads packed per
+// key/value head; 1 when every query head has its own tiles).
 inline bool make_plan(const int32_t* cu, const int32_t* cuk, int n_seg, int H, int block_m,
-                      std::vector<Launch>& out) {
+                      std::vector<Launch>& out, int rows_per_token = 1) {
   struct Seg { int32_t start, len, kstart, klen; int orig; };
   std::vector<Seg> segs;
   segs.reserve(n_seg);
@@ -109,7 +111,7 @@ inline bool make_plan(const int32_t* cu, const int32_t* cuk, int n_seg, int H, i
       l.table.len[j] = s.len;
       l.table.kstart[j] = s.kstart;
       l.table.klen[j] = s.klen;
-      tiles += (s.len + block_m - 1) / block_m;
+      tiles += (static_cast<int64_t>(s.len) * rows_per_token + block_m - 1) / block_m;
       if (tiles * H > std::numeric_limits<int32_t>::max()) return false;
       l.table.tile_prefix[j + 1] = static_cast<int32_t>(tiles);
       l.orig.push_back(s.orig);
