@@ -118,3 +118,23 @@ def test_dense_path_unchanged_by_the_generalisation(torch):
     mg.mgattn_dense(q, k, v, b, cu, 3, H, d, 0.1, 1, wl.BF16, s)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,window", [(64, 16, 2, 0), (96, 8, 1, 100), (128, 32, 2, 2048), (128, 4, 4, 33),
+                                            (64, 32, 1, 1)])
+def test_decode_kernel_shapes(torch, d, Hq, Hkv, window):
+    """One-token decoding (the key-split decode kernel): groupings up to 32 query heads
+    per key/value head, head sizes, windows, caches from 1 to beyond the window."""
+    lk = [1, 2, 31, 32, 33, 255, 700, 2100]
+    _check(torch, "decode kernel", [1] * len(lk), lk, Hq, Hkv, d, window, wl.BF16, seed=871 + d + window)
+
+
+def test_decode_many_sequences_and_scales(torch):
+    """More sequences than one launch holds (150 > 120), empty query rows in between,
+    and negative / zero scale."""
+    rng = np.random.default_rng(881)
+    lk = rng.integers(1, 600, size=150).tolist()
+    lq = [1] * 150
+    lq[3] = 0
+    for scale in (-0.2, 0.0):
+        _check(torch, f"decode 150 seqs scale {scale}", lq, lk, 16, 2, 128, 300, wl.BF16, seed=883, scale=scale)

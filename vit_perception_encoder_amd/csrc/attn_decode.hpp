@@ -1,0 +1,224 @@
+// One-token decoding of the text decoder's attention (mbext next-steps page,
+// "Architecture / Text decoder": grouped key/value heads, a local window of 2048
+// tokens, incremental decoding with a KV cache), bf16, split over the keys.
+//
+// A workgroup = one (sequence, key/value head): the G <= 32 query heads of the group,
+// for the sequence's single new token, are the 32 columns of the score tile (S^T =
+// K Q^T with v_mfma_f32_32x32x16_bf16, columns >= G zero).  The visible keys (the last
+// `window` of the cache, or all of it) are split into contiguous 32-key blocks, and
+// wave w takes the w-th eighth of them: each wave runs its own online softmax over
+// its keys (K operands loaded straight from HBM one block ahead; V blocks staged by
+// LDS DMA into the wave's own double buffer and read transposed with
+// ds_read_b64_tr_b16).  At the end the eight partial results (m, l, O) are merged
+// through LDS: O = sum_w 2^{(m_w - M) c} O_w / sum_w 2^{(m_w - M) c} l_w.
+// K and V of the window are read exactly once; no second pass, no device memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_bf16.hpp"
+#include "plan.hpp"
+
+namespace mgattn {
+
+template <int D>
+struct DecodeTile {
+  static constexpr int kWaves = 8;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBlockElems = 32 * D;                    // one 32-key V block
+  static constexpr int kWaveElems = 2 * kBlockElems;             // double buffer per wave
+  static constexpr int kVBytes = kWaves * kWaveElems * 2;
+  static constexpr int kMergeBytes = kWaves * (D * 32 + 64) * 4;  // O tiles + m, l per wave
+  static constexpr int kLdsBytes = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one CU");
+  static_assert(D % 32 == 0 && D <= 128, "head_dim must be a multiple of 32 up to 128");
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_decode_bf16(KernelArgs a) {
+  using TL = DecodeTile<D>;
+  constexpr int KS = D / 16;  // MFMA k-steps over head_dim
+  constexpr int CT = D / 32;  // 32-channel output tiles
+  constexpr int VDMA = 32 * D / 8 / 64;  // LDS DMA instructions per V block
+  constexpr float kRescaleLog2 = 8.0f;
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kLdsBytes / 2];
+
+  const int Hkv = a.H;  // workgroups per sequence
+  const int slot = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  if (slot >= a.table.n) return;
+  const int G = a.hq_per_kv;
+  const int Lk = a.table.klen[slot];
+  const int k_lo = a.window > 0 ? max(0, Lk - a.window) : 0;  // first visible key
+  const int nblk = (Lk - k_lo + 31) / 32;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;   // score column: query head g*G + n
+  const int hf = lane >> 5;
+  const float c = a.c;
+  // this wave's blocks
+  const int b_begin = nblk * wave / TL::kWaves, b_end = nblk * (wave + 1) / TL::kWaves;
+
+  const __bf16* __restrict__ kg =
+      static_cast<const __bf16*>(a.k) + static_cast<size_t>(a.table.kstart[slot]) * a.ldk + static_cast<size_t>(g) * D;
+  const __bf16* __restrict__ vg =
+      static_cast<const __bf16*>(a.v) + static_cast<size_t>(a.table.kstart[slot]) * a.ldv + static_cast<size_t>(g) * D;
+
+  // Q fragments: column n = query head g*G + n of the sequence's token, channels
+  // 16s + 8hf + [0,8); columns >= G are zero.
+  bf16x8 qf[KS];
+  if (n < G) {
+    const bf16x8* p = reinterpret_cast<const bf16x8*>(
+        static_cast<const __bf16*>(a.q) + static_cast<size_t>(a.table.start[slot]) * a.ldq +
+        static_cast<size_t>(g * G + n) * D + 8 * hf);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = p[2 * s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  if (a.qsign != 1) {
+    const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
+  }
+
+  __bf16* vbuf = lds + wave * TL::kWaveElems;
+  auto key_of = [&](int blk, int i) { return min(k_lo + blk * 32 + i, Lk - 1); };  // clamped row
+  auto load_k = [&](int blk, bf16x8(&kf)[KS]) {
+    const bf16x8* p = reinterpret_cast<const bf16x8*>(kg + static_cast<size_t>(key_of(blk, n)) * a.ldk + 8 * hf);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = p[2 * s];
+  };
+  auto issue_v = [&](int blk) {  // V block -> this wave's buffer blk & 1, row-major, pitch D
+    __bf16* dst = vbuf + (blk & 1) * TL::kBlockElems;
+#pragma unroll
+    for (int u = 0; u < VDMA; ++u) {
+      const int slot16 = u * 64 + lane;
+      dma16(vg + static_cast<size_t>(key_of(blk, slot16 / (D / 8))) * a.ldv + (slot16 % (D / 8)) * 8,
+            __builtin_amdgcn_readfirstlane(lds_addr(dst + u * 512)));
+    }
+  };
+
+  f32x16 o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x16{};
+  float m_run = -1.0e30f, l_run = 0.0f;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  const int tr_row = ((lane & 15) >> 2) + 4 * hf;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  bf16x8 kcur[KS], knext[KS];
+  if (b_begin < b_end) {
+    load_k(b_begin, kcur);
+    issue_v(b_begin);
+  }
+  for (int blk = b_begin; blk < b_end; ++blk) {
+    // block blk's K (registers) and V (this wave's buffer blk & 1) have arrived; the
+    // next block's loads go out now, a whole block of work ahead of their use, and
+    // its V goes to the other buffer, whose last reads were the previous block's
+    dma_wait();
+    const bool more = blk + 1 < b_end;
+    if (more) {
+      load_k(blk + 1, knext);
+      issue_v(blk + 1);
+    }
+    // scores of this block
+    f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qf[0], f32x16{}, 0, 0, 0);
+#pragma unroll
+    for (int st = 1; st < KS; ++st) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[st], qf[st], s, 0, 0, 0);
+    const int key0 = k_lo + blk * 32;
+    if (key0 + 32 > Lk) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (key0 + acc_row(r, hf) >= Lk) s[r] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float m_blk = half_swap_max(mx);
+    if (__builtin_amdgcn_ballot_w64((m_blk - m_run) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+    }
+    const float mc = m_run * c;
+    bf16x8 pk[2];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pk[h2][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h2 + e], c, -mc)));
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pk[h2][e], pk[h2][e + 1]}, ones, lsum, false);
+    }
+    l_run += lsum;
+    const __bf16* vt = vbuf + (blk & 1) * TL::kBlockElems;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const __bf16* vrow = vt + (h2 * 16 + tr_row) * D + tr_col;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const bf16x4 lo = ds_read_tr(vrow + ct * 32);
+        const bf16x4 hi = ds_read_tr(vrow + 8 * D + ct * 32);
+        o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                         pk[h2], o[ct], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) kcur[st] = knext[st];
+  }
+  const float l_all = half_swap_sum(l_run);
+
+  // ---- merge the eight partial results through LDS (the V buffers are dead once
+  // every wave has passed the barrier)
+  __syncthreads();
+  float* mf = reinterpret_cast<float*>(lds);
+  float* m_w = mf;                        // [wave][32]
+  float* l_w = mf + TL::kWaves * 32;      // [wave][32]
+  float* o_w = mf + TL::kWaves * 64;      // [wave][channel][32]
+  if (hf == 0) {
+    m_w[wave * 32 + n] = m_run;
+    l_w[wave * 32 + n] = l_all;
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o_w[(wave * D + ct * 32 + acc_row(r, hf)) * 32 + n] = o[ct][r];
+  __syncthreads();
+  // thread -> (query column, 8 consecutive channels); G*D/8 pieces
+  __bf16* og = static_cast<__bf16*>(a.o) + static_cast<size_t>(a.table.start[slot]) * a.ldo;
+  for (int piece = tid; piece < G * D / 8; piece += TL::kThreads) {
+    const int col = piece / (D / 8), ch0 = (piece % (D / 8)) * 8;
+    float M = -1.0e30f;
+#pragma unroll
+    for (int w = 0; w < TL::kWaves; ++w) M = fmaxf(M, m_w[w * 32 + col]);
+    float den = 0.0f, f[TL::kWaves];
+#pragma unroll
+    for (int w = 0; w < TL::kWaves; ++w) {
+      f[w] = __builtin_amdgcn_exp2f((m_w[w * 32 + col] - M) * c);
+      den += f[w] * l_w[w * 32 + col];
+    }
+    const float inv = 1.0f / den;
+    bf16x8 val;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < TL::kWaves; ++w) acc += f[w] * o_w[(w * D + ch0 + e) * 32 + col];
+      val[e] = static_cast<__bf16>(acc * inv);
+    }
+    *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(g * G + col) * D + ch0) = val;
+  }
+}
+
+}  // namespace mgattn

@@ -17,6 +17,7 @@
 
 #include "../../include/mgattn.h"
 #include "attn_bf16.hpp"
+#include "attn_decode.hpp"
 #include "attn_f32.hpp"
 #include "plan.hpp"
 #include "window_rope.hpp"
@@ -223,6 +224,23 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   args.c = scale == 0.0f ? 1.0f : static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);
   args.qsign = scale > 0.0f ? 1 : (scale < 0.0f ? -1 : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // One-token decoding (every sequence has a single new query): the key-split decode
+  // kernel, one workgroup per (sequence, key/value head).
+  bool decode = pack && H / Hkv <= 32;
+  for (int g = 0; decode && g < n_seg; ++g) decode = cu[g + 1] - cu[g] <= 1;
+  if (decode) {
+    for (const Launch& l : plan) {
+      args.table = l.table;
+      void* params[] = {&args};
+      const void* kern = d == 64 ? reinterpret_cast<const void*>(attn_decode_bf16<64>)
+                         : d == 96 ? reinterpret_cast<const void*>(attn_decode_bf16<96>)
+                                   : reinterpret_cast<const void*>(attn_decode_bf16<128>);
+      if (hipLaunchKernel(kern, dim3(static_cast<unsigned>(l.table.n * Hkv)), dim3(DecodeTile<96>::kThreads), params,
+                          0, s) != hipSuccess)
+        return MGATTN_ERR_LAUNCH;
+    }
+    return MGATTN_OK;
+  }
   if (dtype == MGATTN_BF16) {
     switch (d) {
       case 64:
