@@ -179,6 +179,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch the 50 layers eagerly instead of replaying a graph")
+    ap.add_argument("--no-token-path", action="store_true",
+                    help="skip detail.token_path (profiling runs that count only the tower's launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -281,7 +283,7 @@ def main() -> int:
 
     print("[bench] timing the other entry points (merged qkv, window gather, 2D RoPE, text decoder)", file=sys.stderr,
           flush=True)
-    token = token_path(torch, mg, wl, layers)
+    token = None if args.no_token_path else token_path(torch, mg, wl, layers)
 
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
