@@ -115,11 +115,16 @@ def token_path(torch, mg, wl, layers):
     row = H * d
     stream = torch.cuda.current_stream()
     res = {}
-    # merged qkv, full layer 3
+    # merged qkv, full layer 3, beside the same layer from separate tensors timed the
+    # same way (events around each launch, median)
     q, k, v, cu, nseg, flops, _ = layers[3]
     T = q.shape[0]
-    qkv = torch.cat([q, k, v], dim=1).contiguous()
     out = torch.empty(T, row, dtype=torch.bfloat16, device=dev)
+    ms = time_launches(torch, lambda: mg.mgattn_dense(q, k, v, out, cu, nseg, H, d, wl.SCALE, 0, mg.MGATTN_BF16,
+                                                      stream))
+    res["separate_qkv_full_layer_4096"] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                                           "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    qkv = torch.cat([q, k, v], dim=1).contiguous()
     ms = time_launches(torch, lambda: mg.mgattn_dense_strided(
         qkv[:, :row], qkv[:, row:2 * row], qkv[:, 2 * row:], out, qkv.stride(0), qkv.stride(0), qkv.stride(0),
         row, cu, nseg, H, d, wl.SCALE, 0, mg.MGATTN_BF16, stream))

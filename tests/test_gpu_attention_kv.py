@@ -104,18 +104,21 @@ def test_merged_qkv_text_layout(torch):
     assert np.abs(from_device(out, torch).reshape(T, Hq, d) - want).max() <= BF16_TOL
 
 
-def test_dense_path_unchanged_by_the_generalisation(torch):
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_dense_path_unchanged_by_the_generalisation(torch, dtype, d):
     """mgattn_attention_kv with keys = queries, Hkv = Hq and no window equals the causal
-    dense call bit for bit (one kernel serves both)."""
-    H, d, lens = 4, 96, [333, 64, 1]
+    dense call bit for bit (the same arithmetic, from the general and the dense
+    instantiation of one kernel template)."""
+    H, lens = 4, [333, 64, 1]
     cu = [0] + list(np.cumsum(lens))
     T = cu[-1]
-    say("kv entry vs dense causal")
-    q, k, v = (to_device(_arr(861 + i, (T, H * d), wl.BF16)[0], torch) for i in range(3))
+    say(f"kv entry vs dense causal, dtype={dtype} d={d}")
+    q, k, v = (to_device(_arr(861 + i, (T, H * d), dtype)[0], torch) for i in range(3))
     a, b = torch.empty_like(q), torch.empty_like(q)
     s = torch.cuda.current_stream()
-    mg.mgattn_attention_kv(q, k, v, a, H * d, H * d, H * d, H * d, cu, cu, 3, H, H, d, 0.1, 0, wl.BF16, s)
-    mg.mgattn_dense(q, k, v, b, cu, 3, H, d, 0.1, 1, wl.BF16, s)
+    mg.mgattn_attention_kv(q, k, v, a, H * d, H * d, H * d, H * d, cu, cu, 3, H, H, d, 0.1, 0, dtype, s)
+    mg.mgattn_dense(q, k, v, b, cu, 3, H, d, 0.1, 1, dtype, s)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 

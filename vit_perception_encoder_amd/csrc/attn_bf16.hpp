@@ -27,7 +27,8 @@
 //     The K operands of the next QK product are read from LDS during the softmax
 //     phase, so the MFMA phase issues its QK MFMAs back to back.
 //     K rows are padded to 13 x 16 bytes (pitch 208 B: every 16-byte MFMA operand
-//     read is free of bank conflicts); the padding slots are masked-off lanes.
+//     read is free of bank conflicts); the padding slot of a row receives a second
+//     copy of its last 16 bytes, so every DMA lane is active.
 //   * Softmax (per 64-key step) uses exp2 with scale*log2(e) folded into one FMA per
 //     score.  The running maximum is refreshed only when a step's maximum exceeds it
 //     by more than 2^8 in probability terms (decided per wave), so the O rescale is
@@ -95,6 +96,7 @@ struct Bf16Tile {
   static_assert(kBlockN % kStepKeys == 0 && kStepKeys % 32 == 0, "LDS tile must hold whole softmax steps");
   static_assert((kBlockN * D / 8) % 64 == 0, "V tile must be whole DMA instructions");
   static_assert(kKElems % 8 == 0 && kStageElems % 8 == 0, "LDS regions must stay 16-byte aligned");
+  static_assert(kBlockN * kKSlots % 64 == 0, "K tile must be whole DMA instructions");
 };
 
 // Exchange with lane l^32 and combine (max or sum) -- one v_permlane32_swap.
@@ -125,7 +127,28 @@ __device__ inline uint32_t lds_addr(const void* p) {
 __device__ inline void dma16(const void* g, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory");
 }
+// The same with a wave-uniform base and a per-lane 32-bit byte offset (the scalar-base
+// form): no per-lane 64-bit address arithmetic at issue.
+__device__ inline void dma16s(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(base) : "memory");
+}
 __device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most n (wave-uniform) of this wave's vector-memory operations are
+// outstanding: they complete in issue order, so the older ones are done.  Counts above
+// 8 wait for all.
+__device__ inline void dma_wait_leave(int n) {
+  switch (n) {
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 
 // LDS transpose read: 4 bf16 (see the layout note at the top of this file).
 __device__ inline bf16x4 ds_read_tr(const __bf16* p) {
@@ -153,10 +176,10 @@ void attn_fwd_bf16(KernelArgs a) {
   constexpr int VDMA_W = (VDMA + TL::kWaves - 1) / TL::kWaves;
   constexpr float kRescaleLog2 = 8.0f;  // refresh the running max past 2^8 growth
   static_assert(TL::kQBlocks == 1, "one 32-query block per wave");
-  // K operands of the next QK product are read during the softmax phase, except in the
-  // general head_dim-128 instantiation, where their 64 registers would spill: there
-  // they are read in the MFMA phase that uses them (the tile is resident by then).
-  constexpr bool kPrefetchK = !(kGeneral && D >= 128);
+  // K operands of the next QK product are read during the softmax phase, except at
+  // head_dim 128, where their 64 registers would spill: there they are read in the
+  // MFMA phase that uses them (the tile is resident by then).
+  constexpr bool kPrefetchK = D < 128;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
 
@@ -210,7 +233,7 @@ void attn_fwd_bf16(KernelArgs a) {
 
   // ---- LDS DMA plan.  DMA instruction i of a tile fills 64 consecutive 16-byte
   // slots (1 KB); wave w issues instructions w, w+8, ...  K slot s is row s/KSL,
-  // piece s%KSL (piece D/8 is padding: lane masked off).  V slot s is row s/(D/8),
+  // piece s%KSL (piece D/8 is padding: loaded from piece D/8-1).  V slot s is row s/(D/8),
   // piece s%(D/8).  Rows past the segment end are clamped to its last row: their
   // keys are masked (p = 0) and the clamped data is finite.
   int k_row[KDMA_W], k_off[KDMA_W];
@@ -218,8 +241,8 @@ void attn_fwd_bf16(KernelArgs a) {
   for (int u = 0; u < KDMA_W; ++u) {
     const int slot = (wave + TL::kWaves * u) * 64 + lane;
     const int row = slot / KSL, piece = slot % KSL;
-    k_row[u] = (piece < D / 8 && row < BN) ? row : -1;  // -1: lane idle
-    k_off[u] = piece * 8;
+    k_row[u] = row;
+    k_off[u] = min(piece, D / 8 - 1) * 8;  // the padding slot gets a copy of the last piece
   }
   int v_row[VDMA_W], v_off[VDMA_W];
 #pragma unroll
@@ -228,6 +251,16 @@ void attn_fwd_bf16(KernelArgs a) {
     v_row[u] = slot / (D / 8);
     v_off[u] = (slot % (D / 8)) * 8;
   }
+  // Byte offsets of the slots from the tile's first row, for tiles with BN valid rows
+  // (every tile but a segment's last); a tile lies inside its segment, whose span is
+  // below 2^31 bytes, so the offsets fit 32 bits.
+  uint32_t k_boff[KDMA_W], v_boff[VDMA_W];
+#pragma unroll
+  for (int u = 0; u < KDMA_W; ++u)
+    k_boff[u] = (static_cast<uint32_t>(k_row[u]) * static_cast<uint32_t>(ldk) + k_off[u]) * 2u;
+#pragma unroll
+  for (int u = 0; u < VDMA_W; ++u)
+    v_boff[u] = (static_cast<uint32_t>(v_row[u]) * static_cast<uint32_t>(ldv) + v_off[u]) * 2u;
   auto issue_tile = [&](int t, int part) {  // part: 1 = K, 2 = V, 3 = both
     const int kt0 = kb0 + t * BN;
     const int last = Lk - 1 - kt0;  // last valid row of this tile (>= 0)
@@ -235,14 +268,28 @@ void attn_fwd_bf16(KernelArgs a) {
     const __bf16* vb = vg + static_cast<size_t>(kt0) * ldv;
     __bf16* kl = lds + (t % TL::kStages) * TL::kStageElems;
     __bf16* vl = kl + TL::kKElems;
+    if (last >= BN - 1) {  // wave-uniform: every row valid, precomputed offsets
+#pragma unroll
+      for (int u = 0; u < KDMA_W; ++u) {
+        const int i = wave + TL::kWaves * u;
+        if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA))
+          dma16s(kb, k_boff[u], __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
+      }
+#pragma unroll
+      for (int u = 0; u < VDMA_W; ++u) {
+        const int i = wave + TL::kWaves * u;
+        if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
+          dma16s(vb, v_boff[u], __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
+      }
+      return;
+    }
+    // a segment's last tile: rows past its end are clamped to its last row
 #pragma unroll
     for (int u = 0; u < KDMA_W; ++u) {
       const int i = wave + TL::kWaves * u;
-      if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA)) {
-        if (k_row[u] >= 0)
-          dma16(kb + static_cast<size_t>(min(k_row[u], last)) * ldk + k_off[u],
-                __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
-      }
+      if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA))
+        dma16(kb + static_cast<size_t>(min(k_row[u], last)) * ldk + k_off[u],
+              __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
     }
 #pragma unroll
     for (int u = 0; u < VDMA_W; ++u) {
@@ -376,38 +423,53 @@ void attn_fwd_bf16(KernelArgs a) {
   // 16 bytes per lane; rows past the segment end clamped), together with the first
   // K/V tile.  That stage receives its first tile (tile kStages-1) no earlier than
   // phase 2 (the staging rule below), after barriers that follow every wave's reads
-  // of its Q fragments.
+  // of its Q fragments.  Only the leading group's Q rows and K of tile 0 are waited
+  // for before the first barrier; the trailing group's Q rows and V of tile 0 (first
+  // read in phases 1 and 2) are issued after them and waited for at the end of phase 0.
   constexpr int QDMA = BM * D / 8 / 64;
-  static_assert(QDMA % TL::kWaves == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  constexpr int QDMA_W = QDMA / TL::kWaves;  // per wave: first half rows of waves 0-3, second half 4-7
+  static_assert(QDMA % (2 * TL::kWaves) == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  static_assert(VDMA % TL::kWaves == 0 && N2 - 4 >= 0, "V DMAs split evenly; only tile 0 precedes phase 0");
   __bf16* ql = lds + (TL::kStages - 1) * TL::kStageElems;
+  auto issue_q = [&](int u0, int u1) {
 #pragma unroll
-  for (int u = 0; u < QDMA / TL::kWaves; ++u) {
-    const int i = wave + TL::kWaves * u;
-    const int slot = i * 64 + lane;
-    dma16(qg + row_offset(min(q0 + slot / (D / 8), R - 1), a.ldq) + (slot % (D / 8)) * 8,
-          __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
-  }
-  while (t_issue < ntiles && issue_phase(t_issue) < 0) issue_tile(t_issue++, 3);
+    for (int u = 0; u < QDMA_W; ++u) {
+      if (u < u0 || u >= u1) continue;
+      const int i = wave + TL::kWaves * u;
+      const int slot = i * 64 + lane;
+      dma16(qg + row_offset(min(q0 + slot / (D / 8), R - 1), a.ldq) + (slot % (D / 8)) * 8,
+            __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
+    }
+  };
+  issue_q(0, QDMA_W / 2);
+  issue_tile(0, 1);
+  issue_q(QDMA_W / 2, QDMA_W);
+  issue_tile(0, 2);
+  t_issue = 1;
+  t_wait = 1;
   // With three stages a tile's V goes one phase after its K (spreading the DMA issue
   // over two phases); both are waited for at the same phase end.
   int v_pending = -1;
-  while (t_wait < ntiles && N2 * t_wait - 2 < 0) ++t_wait;
-  dma_wait();
+  dma_wait_leave(QDMA_W / 2 + VDMA / TL::kWaves);
   __syncthreads();
+  // this wave's K DMAs per tile (issued in stage_begin(0) for tile 1 with three stages)
+  const int my_kdma = KDMA / TL::kWaves + (wave < KDMA % TL::kWaves ? 1 : 0);
 
   // ---- Q fragments (B operand of S^T): lane holds query qr, channels 16s + 8hf + [0,8)
+  auto read_q = [&]() {
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(ql + (wave * 32 + n) * D + 16 * s + 8 * hf);
-  if (qr >= R) {
+    for (int s = 0; s < KS; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8*>(ql + (wave * 32 + n) * D + 16 * s + 8 * hf);
+    if (qr >= R) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
-  }
-  if (a.qsign != 1) {
-    const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
+      for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+    }
+    if (a.qsign != 1) {
+      const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
-  }
+      for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
+    }
+  };
   auto stage_begin = [&](int p) {
     if (v_pending >= 0) {
       issue_tile(v_pending, 2);
@@ -424,6 +486,7 @@ void attn_fwd_bf16(KernelArgs a) {
     }
   };
   auto stage_end = [&](int p) {
+    if (p == 0) dma_wait_leave(TL::kStages >= 3 && t_issue >= 2 ? my_kdma : 0);  // Q rows 128.., V of tile 0
     if (t_wait < ntiles && N2 * t_wait - 2 == p) {
       dma_wait();
       ++t_wait;
@@ -438,6 +501,7 @@ void attn_fwd_bf16(KernelArgs a) {
   // groups pass the same 2n+2 barriers.
   const int n_st = nsteps;
   if (wave < 4) {
+    read_q();
     stage_begin(0);
     read_k(0);
     mfma_qk();
@@ -470,6 +534,7 @@ void attn_fwd_bf16(KernelArgs a) {
     stage_begin(0);
     stage_end(0);
     __syncthreads();
+    read_q();
     stage_begin(1);
     read_k(0);
     mfma_qk();
