@@ -169,11 +169,22 @@ def token_path(torch, mg, wl, layers):
     od = torch.empty_like(qd)
     cq = list(range(B + 1))
     ck = [i * Lk for i in range(B + 1)]
+    kv_bytes = B * min(Lk, W) * Hkv * dt * 2 * 2  # the window's K and V, read once
+    # keys split over several workgroups per (sequence, key/value head), partial results
+    # in a workspace (decode kernel + merge kernel), and one workgroup per pair without it
+    wsb = mg.mgattn_attention_kv_workspace(cq, ck, B, Hq, Hkv, dt, W, mg.MGATTN_BF16)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    ms = time_launches(torch, lambda: mg.mgattn_attention_kv_ws(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt,
+                                                               cq, ck, B, Hq, Hkv, dt, dt ** -0.5, W, mg.MGATTN_BF16,
+                                                               ws, wsb, stream))
+    res["text_decode_32x4096_window2048"] = {"ms": ms, "kv_bytes": kv_bytes, "gbs": kv_bytes / (ms * 1e-3) / 1e9,
+                                             "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                             "workspace_bytes": wsb, "launches": 2 if wsb else 1}
     ms = time_launches(torch, lambda: mg.mgattn_attention_kv(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt, cq,
                                                             ck, B, Hq, Hkv, dt, dt ** -0.5, W, mg.MGATTN_BF16, stream))
-    kv_bytes = B * min(Lk, W) * Hkv * dt * 2 * 2  # the window's K and V, read once
-    res["text_decode_32x4096_window2048"] = {"ms": ms, "kv_bytes": kv_bytes, "gbs": kv_bytes / (ms * 1e-3) / 1e9,
-                                             "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    res["text_decode_32x4096_window2048_no_workspace"] = {"ms": ms, "kv_bytes": kv_bytes,
+                                                          "gbs": kv_bytes / (ms * 1e-3) / 1e9,
+                                                          "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return res
 
 

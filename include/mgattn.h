@@ -27,6 +27,7 @@
 #define MGATTN_H
 
 #include <stdint.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -149,6 +150,41 @@ int mgattn_attention_kv(const void* q, const void* k, const void* v, void* out,
                         int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
                         int Hq, int Hkv, int d, float scale, int window, int dtype, void* stream);
+
+/*
+ * mgattn_attention_kv_ws: mgattn_attention_kv with a caller-provided device workspace.
+ * One-token decoding (bf16, every sequence with Lq <= 1, Hq / Hkv <= 32) runs one
+ * workgroup per (sequence, key/value head) in mgattn_attention_kv; with few sequences
+ * that leaves most of the 256 CUs idle while the cache is streamed from HBM.  Given a
+ * workspace, the visible keys of each (sequence, key/value head) are split over up to
+ * 16 workgroups (as many as workspace_bytes holds, toward one workgroup per CU); each
+ * writes its partial result (running maximum, denominator and normalised output, in
+ * f32) to the workspace and a second kernel merges them into out.  The result equals
+ * mgattn_attention_kv's up to the f32 rounding of that merge.  Calls that are not
+ * one-token decoding ignore the workspace.
+ *
+ *   workspace        device, 256-byte aligned, workspace_bytes bytes, overlapping none
+ *                    of q, k, v, out.  Scratch: written and read by the call's kernels
+ *                    in stream order; calls that may overlap in time need distinct
+ *                    workspaces.  The library still allocates no device memory.
+ *   workspace_bytes  0 (workspace may be NULL): exactly mgattn_attention_kv.  A size
+ *                    from mgattn_attention_kv_workspace gives the full split.
+ * Other arguments, checks and return values: mgattn_attention_kv; a misaligned
+ * workspace is MGATTN_ERR_ALIGN, an overlapping one MGATTN_ERR_ALIAS, NULL with
+ * workspace_bytes > 0 MGATTN_ERR_NULL.
+ */
+int mgattn_attention_kv_ws(const void* q, const void* k, const void* v, void* out,
+                           int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
+                           int Hq, int Hkv, int d, float scale, int window, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace with which mgattn_attention_kv_ws splits these arguments fully:
+ * 0 when they are not one-token decoding in bf16 or no split would help.  Pure host
+ * arithmetic, no GPU needed; a negative mgattn_status for malformed arguments (the
+ * host array and shape checks of mgattn_attention_kv). */
+long mgattn_attention_kv_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
+                                   int Hq, int Hkv, int d, int window, int dtype);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* mgattn_strerror(int status);

@@ -233,3 +233,77 @@ def test_attention_kv_null_key_seqlens(lib):
     st = lib.mgattn_attention_kv(Q, K, V, O, 4096, 256, 256, 4096, (ctypes.c_int32 * 2)(0, 10), None, 1, 32, 2, 128,
                                  0.1, 2048, 1, None)
     assert st == -1
+
+
+# ------------------------------------------------- decode workspace (host arithmetic)
+
+def _dec_cu(n, lk):
+    return list(range(n + 1)), [lk * i for i in range(n + 1)]
+
+
+def test_workspace_bytes_of_the_text_decode_shape(lib):
+    """32 sequences decoding one token over 4096 cached keys (32 query, 2 key/value
+    heads, head size 128, window 2048): 64 (sequence, key/value head) pairs split 4
+    ways fill the 256 CUs once; each split holds 32 columns of 128 floats + (M, den)."""
+    cq, ck = _dec_cu(32, 4096)
+    assert mg.mgattn_attention_kv_workspace(cq, ck, 32, 32, 2, 128, 2048, 1) == 32 * 2 * 4 * 32 * (128 + 2) * 4
+
+
+@pytest.mark.parametrize("what,args,want", [
+    ("prefill is not decoding", ([0, 10], [0, 10], 1, 32, 2, 128, 0, 1), 0),
+    ("f32 has no split path", ([0, 1], [0, 4096], 1, 32, 2, 128, 0, 0), 0),
+    # 120 sequences (one launch) x 4 key/value heads = 480 pairs: already one per CU
+    ("enough pairs already", (list(range(121)), [4096 * i for i in range(121)], 120, 32, 4, 128, 0, 1), 0),
+    # 128 sequences: launches of 120 and 8; the 8-sequence launch (16 pairs) is split
+    ("a small second launch is split", (list(range(129)), [4096 * i for i in range(129)], 128, 32, 2, 128, 0, 1),
+     8 * 2 * 16 * 32 * 130 * 4),
+    ("under 8 blocks per split", ([0, 1], [0, 255], 1, 32, 2, 128, 0, 1), 0),
+    ("window caps the visible keys", ([0, 1], [0, 100000], 1, 32, 2, 128, 256, 1), 0),
+    # one pair, 2048 visible keys = 64 blocks: min(256, 64 / 8) = 8 splits
+    ("window 2048, one sequence", ([0, 1], [0, 100000], 1, 32, 2, 128, 2048, 1), 2 * 8 * 32 * 130 * 4),
+    # 2 pairs, 20000 keys = 625 blocks: min(128, 78, 16) = 16 splits
+    ("split count capped at 16", ([0, 1], [0, 20000], 1, 8, 2, 64, 0, 1), 2 * 16 * 32 * 66 * 4),
+])
+def test_workspace_bytes_rules(lib, what, args, want):
+    assert mg.mgattn_attention_kv_workspace(*args) == want, what
+
+
+@pytest.mark.parametrize("args,status", [
+    (([0, 1], [0, 10], 1, 32, 3, 128, 0, 1), -4),
+    (([0, 1], [0, 10], 1, 32, 2, 128, -1, 1), -15),
+    (([0, 1], [0, 10], 1, 32, 2, 80, 0, 1), -3),
+    (([0, 1], [0, 10], 1, 32, 2, 128, 0, 7), -2),
+    (([0, 2], [0, 1], 1, 32, 2, 128, 0, 1), -5),   # fewer keys than queries
+    (([1, 2], [0, 10], 1, 32, 2, 128, 0, 1), -5),
+    (([0, 1], [0, 10], 0, 32, 2, 128, 0, 1), -6),
+])
+def test_workspace_bytes_refusals(lib, args, status):
+    assert mg.mgattn_attention_kv_workspace(*args) == status
+
+
+def test_workspace_bytes_null_seqlens(lib):
+    vp = ctypes.c_void_p
+    assert lib.mgattn_attention_kv_workspace(None, vp(0), 1, 32, 2, 128, 0, 1) == -1
+
+
+WS = 0x800000
+
+
+@pytest.mark.parametrize("ws,nbytes,kw,status", [
+    (WS + 16, 4096, {}, -8),           # workspace not 256-byte aligned
+    (None, 4096, {}, -1),              # NULL with a size
+    (K, 4096, {}, -7),                 # workspace overlaps k
+    (O - 256, 4096, {}, -7),           # ... and out
+    (WS, 4096, dict(Hkv=3), -4),       # every mgattn_attention_kv check still applies
+    (WS, 4096, dict(window=-1), -15),
+    (WS, 4096, dict(o=K + 16), -7),
+])
+def test_attention_kv_ws_refusals(lib, ws, nbytes, kw, status):
+    a = dict(cq=(0, 1, 2), ck=(0, 20, 50), Hq=32, Hkv=2, d=128, window=2048)
+    a.update(kw)
+    o = a.pop("o", O)
+    cq, ck = a["cq"], a["ck"]
+    Hq, Hkv, d = a["Hq"], a["Hkv"], a["d"]
+    st = mg.mgattn_attention_kv_ws(Q, K, V, o, Hq * d, Hkv * d, Hkv * d, Hq * d, list(cq), list(ck), len(cq) - 1, Hq,
+                                   Hkv, d, 0.1, a["window"], 1, ws, nbytes, None, check=False)
+    assert st == status

@@ -141,3 +141,86 @@ def test_decode_many_sequences_and_scales(torch):
     lq[3] = 0
     for scale in (-0.2, 0.0):
         _check(torch, f"decode 150 seqs scale {scale}", lq, lk, 16, 2, 128, 300, wl.BF16, seed=883, scale=scale)
+
+
+# ------------------------------------------------ one-token decoding with a workspace
+
+def _check_ws(torch, name, lk, Hq, Hkv, d, window, seed, ws_frac=1.0, scale=None, expect_split=True, ws=None):
+    """mgattn_attention_kv_ws on one-token decoding against the oracle, with a workspace
+    of ws_frac times the full-split size (in the tensor ws when given)."""
+    n = len(lk)
+    cq = np.arange(n + 1, dtype=np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    full = mg.mgattn_attention_kv_workspace(list(cq), list(ck), n, Hq, Hkv, d, window, wl.BF16)
+    assert (full > 0) == expect_split, full
+    nbytes = int(full * ws_frac) // 256 * 256
+    say(f"{name}: n={n} lk[:8]={lk[:8]} Hq={Hq} Hkv={Hkv} d={d} window={window} workspace={nbytes}/{full}")
+    q, qf = _arr(seed, (n, Hq * d), wl.BF16)
+    k, kf = _arr(seed + 1, (int(ck[-1]), Hkv * d), wl.BF16)
+    v, vf = _arr(seed + 2, (int(ck[-1]), Hkv * d), wl.BF16)
+    qd, kd, vd = (to_device(x, torch) for x in (q, k, v))
+    out = torch.full_like(qd, -777.0)
+    if ws is None:
+        ws = torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device="cuda")  # NaN-patterned scratch
+    assert ws.numel() >= nbytes
+    mg.mgattn_attention_kv_ws(qd, kd, vd, out, Hq * d, Hkv * d, Hkv * d, Hq * d, list(cq), list(ck), n, Hq, Hkv, d,
+                              scale, window, wl.BF16, ws, nbytes, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got = from_device(out, torch).reshape(n, Hq, d)
+    want = G.attention_kv(qf, kf, vf, cq, ck, Hq, Hkv, d, scale, window)
+    err = np.abs(got - want)
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    assert np.all(np.isfinite(got))
+    assert err.max() <= BF16_TOL, f"max err {err.max():.3e} at (seq,h,c)={worst}"
+    return got
+
+
+def test_decode_split_text_decoder_batch(torch):
+    """The text decoder's decoding step at batch 32 over 4096 cached keys (window 2048):
+    64 (sequence, key/value head) pairs, each split over 4 workgroups."""
+    _check_ws(torch, "decode split 32x4096", [4096] * 32, 32, 2, 128, 2048, seed=891)
+
+
+@pytest.mark.parametrize("d,Hq,Hkv,window", [(64, 16, 2, 0), (96, 8, 1, 100), (128, 32, 2, 2048), (128, 4, 4, 33),
+                                            (64, 32, 1, 1), (128, 32, 2, 0)])
+def test_decode_split_shapes(torch, d, Hq, Hkv, window):
+    """Split decoding with caches from 1 key (splits without keys) to beyond the
+    window, every grouping and head size of the unsplit kernel's test."""
+    lk = [1, 2, 31, 33, 255, 700, 2100, 5000]
+    _check_ws(torch, "decode split", lk, Hq, Hkv, d, window, seed=901 + d + window,
+              expect_split=window in (0, 2048))  # smaller windows leave < 16 blocks: no split
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.3, 0.5, 1.0])
+def test_decode_split_partial_workspace(torch, frac):
+    """A workspace below the full size gives fewer splits (none at 0 bytes), same result."""
+    _check_ws(torch, f"decode workspace x{frac}", [3000, 17, 900], 32, 2, 128, 0, seed=911, ws_frac=frac)
+
+
+def test_decode_split_scales_and_reuse(torch):
+    """Negative and zero scale, and two calls in a row sharing one workspace (the second
+    with fewer, shorter sequences)."""
+    for scale in (-0.2, 0.0):
+        _check_ws(torch, f"decode split scale {scale}", [1500, 2500, 64], 16, 2, 128, 2048, seed=921, scale=scale)
+    ws = torch.full((8 << 20,), 0xFF, dtype=torch.uint8, device="cuda")
+    _check_ws(torch, "decode split reuse 1", [4000] * 6, 32, 2, 128, 0, seed=923, ws=ws)
+    _check_ws(torch, "decode split reuse 2", [700, 1200], 32, 2, 128, 0, seed=925, ws=ws)
+
+
+def test_decode_without_workspace_is_the_plain_entry(torch):
+    """workspace_bytes = 0 runs exactly mgattn_attention_kv (bit for bit)."""
+    lk = [4096] * 4
+    n, Hq, Hkv, d = 4, 32, 2, 128
+    cq, ck = list(range(n + 1)), [4096 * i for i in range(n + 1)]
+    q = to_device(_arr(931, (n, Hq * d), wl.BF16)[0], torch)
+    k = to_device(_arr(932, (sum(lk), Hkv * d), wl.BF16)[0], torch)
+    v = to_device(_arr(933, (sum(lk), Hkv * d), wl.BF16)[0], torch)
+    a, b = torch.empty_like(q), torch.empty_like(q)
+    s = torch.cuda.current_stream()
+    say("decode ws=0 vs plain")
+    mg.mgattn_attention_kv(q, k, v, a, Hq * d, Hkv * d, Hkv * d, Hq * d, cq, ck, n, Hq, Hkv, d, 0.09, 2048, wl.BF16, s)
+    mg.mgattn_attention_kv_ws(q, k, v, b, Hq * d, Hkv * d, Hkv * d, Hq * d, cq, ck, n, Hq, Hkv, d, 0.09, 2048, wl.BF16,
+                              None, 0, s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -68,6 +68,8 @@ struct KernelArgs {
   int32_t ldq, ldk, ldv, ldo;  // elements between consecutive tokens of q, k, v, out
   int32_t hq_per_kv;  // query heads per key/value head (1 without grouping)
   int32_t window;     // causal sliding window in keys, the query's own included (0: none)
+  int32_t nsplit;     // one-token decoding: workgroups per (sequence, key/value head)
+  float* part;        // nsplit > 1: partial results of the key splits (caller's workspace)
   SegTable table;
 };
 
@@ -135,20 +137,19 @@ __device__ inline void dma16s(const void* base, uint32_t off, uint32_t m0) {
 __device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most n (wave-uniform) of this wave's vector-memory operations are
 // outstanding: they complete in issue order, so the older ones are done.  Counts above
-// 8 wait for all.
+// 16 wait for all.
+#define MGATTN_VMCNT_CASE(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
 __device__ inline void dma_wait_leave(int n) {
   switch (n) {
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    MGATTN_VMCNT_CASE(1) MGATTN_VMCNT_CASE(2) MGATTN_VMCNT_CASE(3) MGATTN_VMCNT_CASE(4)
+    MGATTN_VMCNT_CASE(5) MGATTN_VMCNT_CASE(6) MGATTN_VMCNT_CASE(7) MGATTN_VMCNT_CASE(8)
+    MGATTN_VMCNT_CASE(9) MGATTN_VMCNT_CASE(10) MGATTN_VMCNT_CASE(11) MGATTN_VMCNT_CASE(12)
+    MGATTN_VMCNT_CASE(13) MGATTN_VMCNT_CASE(14) MGATTN_VMCNT_CASE(15) MGATTN_VMCNT_CASE(16)
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }
+#undef MGATTN_VMCNT_CASE
 
 // LDS transpose read: 4 bf16 (see the layout note at the top of this file).
 __device__ inline bf16x4 ds_read_tr(const __bf16* p) {

@@ -11,7 +11,13 @@
 // LDS DMA into the wave's own double buffer and read transposed with
 // ds_read_b64_tr_b16).  At the end the eight partial results (m, l, O) are merged
 // through LDS: O = sum_w 2^{(m_w - M) c} O_w / sum_w 2^{(m_w - M) c} l_w.
-// K and V of the window are read exactly once; no second pass, no device memory.
+// K and V of the window are read exactly once.
+//
+// With few sequences (n_seq * Hkv well below the 256 CUs) the keys are further split
+// over nsplit workgroups per (sequence, key/value head), each taking a contiguous
+// range of blocks; they write their merged (M, den, O / den) to a caller-provided
+// workspace in f32, and attn_decode_combine merges the nsplit partial results the
+// same way (weights 2^{(M_s - M) c} den_s) into the bf16 output.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -46,13 +52,18 @@ void attn_decode_bf16(KernelArgs a) {
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kLdsBytes / 2];
 
-  const int Hkv = a.H;  // workgroups per sequence
-  const int slot = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int Hkv = a.H;  // key/value heads
+  const int nsplit = a.nsplit;
+  const int wg = blockIdx.x / nsplit, split = blockIdx.x % nsplit;  // wg = (sequence, key/value head)
+  const int slot = wg / Hkv, g = wg % Hkv;
   if (slot >= a.table.n) return;
   const int G = a.hq_per_kv;
   const int Lk = a.table.klen[slot];
   const int k_lo = a.window > 0 ? max(0, Lk - a.window) : 0;  // first visible key
-  const int nblk = (Lk - k_lo + 31) / 32;
+  const int nblk_all = (Lk - k_lo + 31) / 32;
+  // this workgroup's blocks: [sb0, sb0 + nblk) (possibly none when nsplit > 1)
+  const int sb0 = nblk_all * split / nsplit;
+  const int nblk = nblk_all * (split + 1) / nsplit - sb0;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -61,7 +72,7 @@ void attn_decode_bf16(KernelArgs a) {
   const int hf = lane >> 5;
   const float c = a.c;
   // this wave's blocks
-  const int b_begin = nblk * wave / TL::kWaves, b_end = nblk * (wave + 1) / TL::kWaves;
+  const int b_begin = sb0 + nblk * wave / TL::kWaves, b_end = sb0 + nblk * (wave + 1) / TL::kWaves;
 
   const __bf16* __restrict__ kg =
       static_cast<const __bf16*>(a.k) + static_cast<size_t>(a.table.kstart[slot]) * a.ldk + static_cast<size_t>(g) * D;
@@ -112,21 +123,22 @@ void attn_decode_bf16(KernelArgs a) {
   const int tr_row = ((lane & 15) >> 2) + 4 * hf;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
+  // Two blocks in flight: blocks b and b+1 are loaded before block b is waited for
+  // (counted: block b+1's KS K loads and VDMA V copies may still be outstanding), and
+  // block b+2 goes out once block b's operands are consumed -- its V into the buffer
+  // block b just vacated.
   bf16x8 kcur[KS], knext[KS];
   if (b_begin < b_end) {
     load_k(b_begin, kcur);
     issue_v(b_begin);
   }
+  if (b_begin + 1 < b_end) {
+    load_k(b_begin + 1, knext);
+    issue_v(b_begin + 1);
+  }
   for (int blk = b_begin; blk < b_end; ++blk) {
-    // block blk's K (registers) and V (this wave's buffer blk & 1) have arrived; the
-    // next block's loads go out now, a whole block of work ahead of their use, and
-    // its V goes to the other buffer, whose last reads were the previous block's
-    dma_wait();
     const bool more = blk + 1 < b_end;
-    if (more) {
-      load_k(blk + 1, knext);
-      issue_v(blk + 1);
-    }
+    dma_wait_leave(more ? KS + VDMA : 0);
     // scores of this block
     f32x16 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[0], qf[0], f32x16{}, 0, 0, 0);
 #pragma unroll
@@ -176,6 +188,10 @@ void attn_decode_bf16(KernelArgs a) {
     }
 #pragma unroll
     for (int st = 0; st < KS; ++st) kcur[st] = knext[st];
+    if (blk + 2 < b_end) {
+      load_k(blk + 2, knext);
+      issue_v(blk + 2);
+    }
   }
   const float l_all = half_swap_sum(l_run);
 
@@ -208,15 +224,88 @@ void attn_decode_bf16(KernelArgs a) {
       f[w] = __builtin_amdgcn_exp2f((m_w[w * 32 + col] - M) * c);
       den += f[w] * l_w[w * 32 + col];
     }
-    const float inv = 1.0f / den;
-    bf16x8 val;
+    float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float acc = 0.0f;
+      acc[e] = 0.0f;
 #pragma unroll
-      for (int w = 0; w < TL::kWaves; ++w) acc += f[w] * o_w[(w * D + ch0 + e) * 32 + col];
-      val[e] = static_cast<__bf16>(acc * inv);
+      for (int w = 0; w < TL::kWaves; ++w) acc[e] += f[w] * o_w[(w * D + ch0 + e) * 32 + col];
     }
+    if (nsplit == 1) {
+      const float inv = 1.0f / den;
+      bf16x8 val;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[e] = static_cast<__bf16>(acc[e] * inv);
+      *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(g * G + col) * D + ch0) = val;
+    } else {
+      // partial result of this split: O / den (0 for a split without keys), M, den
+      const size_t ps = static_cast<size_t>(wg) * nsplit + split;
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      f32x4* po = reinterpret_cast<f32x4*>(a.part + (ps * 32 + col) * D + ch0);
+      po[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+      po[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+      if (ch0 == 0) {
+        float* ml = a.part + static_cast<size_t>(a.table.n) * Hkv * nsplit * 32 * D + ps * 64;
+        ml[col] = M;
+        ml[32 + col] = den;
+      }
+    }
+  }
+}
+
+// Merge of the nsplit (<= kMaxSplit) partial results of one (sequence, key/value head):
+// one workgroup of 256 threads, a thread per (query head of the group, 8 channels).
+constexpr int kMaxSplit = 16;
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void attn_decode_combine(KernelArgs a) {
+  const int Hkv = a.H;
+  const int nsplit = a.nsplit;
+  const int wg = blockIdx.x;
+  const int slot = wg / Hkv, g = wg % Hkv;
+  if (slot >= a.table.n) return;
+  const int G = a.hq_per_kv;
+  const float c = a.c;
+  const float* part_o = a.part;
+  const float* part_ml = a.part + static_cast<size_t>(a.table.n) * Hkv * nsplit * 32 * D;
+  __bf16* og = static_cast<__bf16*>(a.o) + static_cast<size_t>(a.table.start[slot]) * a.ldo;
+  for (int piece = threadIdx.x; piece < G * D / 8; piece += 256) {
+    const int col = piece / (D / 8), ch0 = (piece % (D / 8)) * 8;
+    // every load of the piece is issued before any is used (splits unrolled up to the
+    // maximum, predicated), so the merge costs one memory round trip
+    float Ms[kMaxSplit], dens[kMaxSplit];
+    f32x4 x0[kMaxSplit], x1[kMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      if (sp < nsplit) {
+        const size_t ps = static_cast<size_t>(wg) * nsplit + sp;
+        Ms[sp] = part_ml[ps * 64 + col];
+        dens[sp] = part_ml[ps * 64 + 32 + col];
+        const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (ps * 32 + col) * D + ch0);
+        x0[sp] = po[0];
+        x1[sp] = po[1];
+      }
+    }
+    float M = -1.0e30f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp)
+      if (sp < nsplit) M = fmaxf(M, Ms[sp]);
+    float tot = 0.0f, acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      if (sp < nsplit) {
+        const float F = __builtin_amdgcn_exp2f((Ms[sp] - M) * c) * dens[sp];
+        tot += F;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] += F * x0[sp][e];
+          acc[4 + e] += F * x1[sp][e];
+        }
+      }
+    }
+    const float inv = 1.0f / tot;
+    bf16x8 val;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] = static_cast<__bf16>(acc[e] * inv);
     *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(g * G + col) * D + ch0) = val;
   }
 }

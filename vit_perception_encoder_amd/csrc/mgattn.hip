@@ -183,16 +183,44 @@ int blocks_for(int64_t items, unsigned* grid) {
 
 }  // namespace
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
+
+// One-token decoding splits a (sequence, key/value head) over several workgroups when
+// the launch has fewer of them than the chip has CUs: as many splits as keep the
+// workgroups within one per CU (more would only add rounds), each split with at least
+// one 32-key block per wave, at most 16.
+constexpr int kDecodeTargetWgs = 256;
+constexpr int kMaxDecodeSplit = kMaxSplit;
+
+int decode_split_wanted(const SegTable& t, int Hkv, int window) {
+  const int wgs = t.n * Hkv;
+  int max_blk = 0;
+  for (int j = 0; j < t.n; ++j) {
+    const int vis = window > 0 ? std::min(t.klen[j], window) : t.klen[j];
+    max_blk = std::max(max_blk, (vis + 31) / 32);
+  }
+  int ns = kDecodeTargetWgs / wgs;
+  ns = std::min(ns, std::max(1, max_blk / DecodeTile<64>::kWaves));
+  return std::max(1, std::min(ns, kMaxDecodeSplit));
+}
+
+// Workspace bytes of the partial results of one launch split nsplit ways: per
+// (sequence, key/value head, split) 32 query columns of d floats plus (M, den).
+size_t decode_part_bytes(const SegTable& t, int Hkv, int nsplit, int d) {
+  return static_cast<size_t>(t.n) * Hkv * nsplit * 32 * (static_cast<size_t>(d) + 2) * sizeof(float);
+}
+
+// Is this call one-token decoding (served by the decode kernel)?
+bool is_decode(const int32_t* cu, int n_seg, int H, int Hkv, bool pack) {
+  bool decode = pack && H / Hkv <= 32;
+  for (int g = 0; decode && g < n_seg; ++g) decode = cu[g + 1] - cu[g] <= 1;
+  return decode;
+}
 
 // Validation, plan and launches shared by every attention entry point.
 int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
            int64_t ldo, const int32_t* cu, const int32_t* cuk, int n_seg, int H, int Hkv, int d, float scale,
-           int causal, int window, int dtype, void* stream) {
+           int causal, int window, int dtype, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
   const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu, cuk, n_seg, H, Hkv, d, scale, causal, window, dtype);
   if (st != MGATTN_OK) return st;
   // The general bf16 kernel packs the query heads of a key/value head into one tile's
@@ -225,19 +253,29 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   args.qsign = scale > 0.0f ? 1 : (scale < 0.0f ? -1 : 0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // One-token decoding (every sequence has a single new query): the key-split decode
-  // kernel, one workgroup per (sequence, key/value head).
-  bool decode = pack && H / Hkv <= 32;
-  for (int g = 0; decode && g < n_seg; ++g) decode = cu[g + 1] - cu[g] <= 1;
-  if (decode) {
+  // kernel, nsplit workgroups per (sequence, key/value head); nsplit > 1 only with a
+  // caller's workspace large enough for the partial results, merged by a second
+  // kernel.  Launches run in stream order, so each reuses the workspace.
+  if (is_decode(cu, n_seg, H, Hkv, pack)) {
     for (const Launch& l : plan) {
       args.table = l.table;
+      int ns = ws ? decode_split_wanted(l.table, Hkv, window) : 1;
+      while (ns > 1 && decode_part_bytes(l.table, Hkv, ns, d) > ws_bytes) --ns;
+      args.nsplit = ns;
+      args.part = ns > 1 ? static_cast<float*>(ws) : nullptr;
       void* params[] = {&args};
       const void* kern = d == 64 ? reinterpret_cast<const void*>(attn_decode_bf16<64>)
                          : d == 96 ? reinterpret_cast<const void*>(attn_decode_bf16<96>)
                                    : reinterpret_cast<const void*>(attn_decode_bf16<128>);
-      if (hipLaunchKernel(kern, dim3(static_cast<unsigned>(l.table.n * Hkv)), dim3(DecodeTile<96>::kThreads), params,
-                          0, s) != hipSuccess)
+      const unsigned wgs = static_cast<unsigned>(l.table.n * Hkv);
+      if (hipLaunchKernel(kern, dim3(wgs * ns), dim3(DecodeTile<96>::kThreads), params, 0, s) != hipSuccess)
         return MGATTN_ERR_LAUNCH;
+      if (ns > 1) {
+        const void* comb = d == 64 ? reinterpret_cast<const void*>(attn_decode_combine<64>)
+                           : d == 96 ? reinterpret_cast<const void*>(attn_decode_combine<96>)
+                                     : reinterpret_cast<const void*>(attn_decode_combine<128>);
+        if (hipLaunchKernel(comb, dim3(wgs), dim3(256), params, 0, s) != hipSuccess) return MGATTN_ERR_LAUNCH;
+      }
     }
     return MGATTN_OK;
   }
@@ -280,6 +318,55 @@ int mgattn_attention_kv(const void* q, const void* k, const void* v, void* out, 
   if (!cu_seqlens_k) return MGATTN_ERR_NULL;
   return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1, window,
                 dtype, stream);
+}
+
+long mgattn_attention_kv_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq, int Hq,
+                                   int Hkv, int d, int window, int dtype) {
+  if (!cu_seqlens_q || !cu_seqlens_k) return MGATTN_ERR_NULL;
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  if (n_seq < 1) return MGATTN_ERR_SEGMENTS;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return MGATTN_ERR_HEADS;
+  if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
+  if (window < 0) return MGATTN_ERR_WINDOW;
+  int64_t Tq = 0, Tk = 0, mq = 0, mk = 0;
+  int st = check_seqlens(cu_seqlens_q, n_seq, &Tq, &mq);
+  if (st != MGATTN_OK) return st;
+  st = check_seqlens(cu_seqlens_k, n_seq, &Tk, &mk);
+  if (st != MGATTN_OK) return st;
+  for (int g = 0; g < n_seq; ++g)
+    if (cu_seqlens_k[g + 1] - cu_seqlens_k[g] < cu_seqlens_q[g + 1] - cu_seqlens_q[g]) return MGATTN_ERR_SEQLENS;
+  if (!is_decode(cu_seqlens_q, n_seq, Hq, Hkv, dtype == MGATTN_BF16)) return 0;
+  std::vector<Launch> plan;
+  if (!make_plan(cu_seqlens_q, cu_seqlens_k, n_seq, Hkv, block_m_of(d, dtype), plan, Hq / Hkv)) return MGATTN_ERR_SIZE;
+  size_t need = 0;
+  for (const Launch& l : plan) {
+    const int ns = decode_split_wanted(l.table, Hkv, window);
+    if (ns > 1) need = std::max(need, decode_part_bytes(l.table, Hkv, ns, d));
+  }
+  return static_cast<long>(need);
+}
+
+int mgattn_attention_kv_ws(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk,
+                           int64_t ldv, int64_t ldo, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int n_seq, int Hq, int Hkv, int d, float scale, int window, int dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens_k || (workspace_bytes > 0 && !workspace)) return MGATTN_ERR_NULL;
+  if (workspace_bytes == 0)
+    return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1, window,
+                  dtype, stream);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MGATTN_ERR_ALIGN;
+  const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1,
+                          window, dtype);
+  if (st != MGATTN_OK) return st;
+  // the workspace may not share bytes with any tensor
+  const int64_t Tq = cu_seqlens_q[n_seq], Tk = cu_seqlens_k[n_seq];
+  if (overlaps(workspace, workspace_bytes, q, span_bytes(Tq, ldq, Hq, d, dtype)) ||
+      overlaps(workspace, workspace_bytes, out, span_bytes(Tq, ldo, Hq, d, dtype)) ||
+      overlaps(workspace, workspace_bytes, k, span_bytes(Tk, ldk, Hkv, d, dtype)) ||
+      overlaps(workspace, workspace_bytes, v, span_bytes(Tk, ldv, Hkv, d, dtype)))
+    return MGATTN_ERR_ALIAS;
+  return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1, window,
+                dtype, stream, workspace, workspace_bytes);
 }
 
 int mgattn_dense(const void* q, const void* k, const void* v, void* out, const int32_t* cu_seqlens,

@@ -26,7 +26,8 @@ STATUS_NAMES = {
     -14: "MGATTN_ERR_GRID", -15: "MGATTN_ERR_WINDOW",
 }
 
-EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_attention_kv", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
+EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_attention_kv", "mgattn_attention_kv_ws",
+           "mgattn_attention_kv_workspace", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
            "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
            "mgattn_window_permute", "mgattn_rope2d", "mgattn_version"]
 
@@ -58,6 +59,11 @@ def load_library(path: str | os.PathLike | None = None):
     lib.mgattn_attention_kv.restype = i32
     lib.mgattn_attention_kv.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i32, i32, i32, i32, f32, i32,
                                         i32, vp]
+    lib.mgattn_attention_kv_ws.restype = i32
+    lib.mgattn_attention_kv_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i32, i32, i32, i32, f32, i32,
+                                           i32, vp, ctypes.c_size_t, vp]
+    lib.mgattn_attention_kv_workspace.restype = ctypes.c_long
+    lib.mgattn_attention_kv_workspace.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32]
     lib.mgattn_strerror.restype = ctypes.c_char_p
     lib.mgattn_strerror.argtypes = [i32]
     lib.mgattn_dense_supported.restype = i32
@@ -154,6 +160,40 @@ def mgattn_attention_kv(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu
     if check and st != 0:
         raise MgattnError(st, "mgattn_attention_kv")
     return st
+
+
+def mgattn_attention_kv_ws(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu_seqlens_q: Sequence[int],
+                           cu_seqlens_k: Sequence[int], n_seq: int, Hq: int, Hkv: int, d: int, scale: float,
+                           window: int, dtype: int, workspace, workspace_bytes: int, stream=None,
+                           check: bool = True) -> int:
+    """mgattn_attention_kv with a caller-provided device workspace, used to split
+    one-token decoding over more workgroups (see mgattn_attention_kv_ws in
+    include/mgattn.h)."""
+    lib = load_library()
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_k)
+    if nq < n_seq + 1 or nk < n_seq + 1:
+        raise ValueError(f"cu_seqlens_q/k need {n_seq + 1} entries")
+    st = lib.mgattn_attention_kv_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
+                                    ctypes.cast(cq, ctypes.c_void_p), ctypes.cast(ck, ctypes.c_void_p), int(n_seq),
+                                    int(Hq), int(Hkv), int(d), float(scale), int(window), int(dtype), _ptr(workspace),
+                                    int(workspace_bytes), _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_attention_kv_ws")
+    return st
+
+
+def mgattn_attention_kv_workspace(cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int], n_seq: int, Hq: int,
+                                  Hkv: int, d: int, window: int, dtype: int) -> int:
+    """Workspace bytes mgattn_attention_kv_ws would use (0: no split), or a negative
+    status.  Host arithmetic only."""
+    lib = load_library()
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_k)
+    if nq < n_seq + 1 or nk < n_seq + 1:
+        raise ValueError(f"cu_seqlens_q/k need {n_seq + 1} entries")
+    return int(lib.mgattn_attention_kv_workspace(ctypes.cast(cq, ctypes.c_void_p), ctypes.cast(ck, ctypes.c_void_p),
+                                                 int(n_seq), int(Hq), int(Hkv), int(d), int(window), int(dtype)))
 
 
 def mgattn_strerror(status: int) -> str:
