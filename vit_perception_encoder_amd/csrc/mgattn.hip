@@ -174,17 +174,6 @@ int make_images(const int32_t* grids, int n_img, ImageTable* tb) {
   return MGATTN_OK;
 }
 
-int blocks_for(int64_t items, unsigned* grid) {
-  const int64_t b = (items + 255) / 256;
-  if (b < 1 || b > INT32_MAX) return MGATTN_ERR_SIZE;
-  *grid = static_cast<unsigned>(b);
-  return MGATTN_OK;
-}
-
-}  // namespace
-
-namespace {
-
 // One-token decoding splits a (sequence, key/value head) over several workgroups when
 // the launch has fewer of them than the chip has CUs: as many splits as keep the
 // workgroups within one per CU (more would only add rounds), each split with at least
@@ -487,15 +476,13 @@ int mgattn_window_permute(const void* src, void* dst, int64_t row_bytes, const i
   const int64_t T = tb.start[n_img];
   const size_t bytes = static_cast<size_t>(T) * static_cast<size_t>(row_bytes);
   if (overlaps(src, bytes, dst, bytes)) return MGATTN_ERR_ALIAS;
-  const int64_t pieces = T * (row_bytes / 16);
-  unsigned grid = 0;
-  if (blocks_for(pieces, &grid) != MGATTN_OK) return MGATTN_ERR_SIZE;
+  // one wave per row, four rows per workgroup
+  const unsigned grid = static_cast<unsigned>((T + 3) / 4);
   if (!device_ok()) return MGATTN_ERR_DEVICE;
   const uint4* s = static_cast<const uint4*>(src);
   uint4* d = static_cast<uint4*>(dst);
-  int32_t ppr = static_cast<int32_t>(row_bytes / 16), w = win, inv = inverse;
-  int64_t total = pieces;
-  void* params[] = {&s, &d, &ppr, &w, &inv, &total, &tb};
+  int32_t ppr = static_cast<int32_t>(row_bytes / 16), w = win, inv = inverse, rows = static_cast<int32_t>(T);
+  void* params[] = {&s, &d, &ppr, &w, &inv, &rows, &tb};
   return hipLaunchKernel(reinterpret_cast<const void*>(window_permute_kernel), dim3(grid), dim3(256), params, 0,
                          static_cast<hipStream_t>(stream)) == hipSuccess
              ? MGATTN_OK
@@ -525,15 +512,14 @@ int mgattn_rope2d(void* x, int64_t ldx, const int32_t* grids, int n_img, int win
   a.d = d;
   a.win = win;
   a.pieces = static_cast<int32_t>(static_cast<int64_t>(d) * static_cast<int64_t>(elem_size(dtype)) / 16);
-  a.groups = (H + kRopeHeadGroup - 1) / kRopeHeadGroup;
   for (int i = 0; i < d / 4; ++i)
     a.inv_freq[i] = static_cast<float>(pow(static_cast<double>(theta), -4.0 * i / d));
   a.tb = tb;
-  int64_t threads = static_cast<int64_t>(tb.start[n_img]) * a.pieces * a.groups;
-  unsigned grid = 0;
-  if (blocks_for(threads, &grid) != MGATTN_OK) return MGATTN_ERR_SIZE;
+  // one wave per token, four tokens per workgroup (tokens < 2^31: make_images)
+  int32_t n_tokens = tb.start[n_img];
+  const unsigned grid = static_cast<unsigned>((static_cast<int64_t>(n_tokens) + 3) / 4);
   if (!device_ok()) return MGATTN_ERR_DEVICE;
-  void* params[] = {&a, &threads};
+  void* params[] = {&a, &n_tokens};
   const void* kern = dtype == MGATTN_BF16 ? reinterpret_cast<const void*>(rope2d_kernel<__bf16>)
                                           : reinterpret_cast<const void*>(rope2d_kernel<float>);
   return hipLaunchKernel(kern, dim3(grid), dim3(256), params, 0, static_cast<hipStream_t>(stream)) == hipSuccess

@@ -62,21 +62,33 @@ __device__ inline int window_to_raster(int p, int gh, int gw, int win) {
 }
 
 // dst row p <- src row perm(p) (gather into window order), or dst row perm(p) <- src
-// row p (inverse: back to raster order).  One 16-byte piece per thread.
+// row p (inverse: back to raster order).  One wave per row p: the row's partner
+// (image, window order <-> raster) is wave-uniform and computed once; the lanes copy
+// the row's 16-byte pieces, four loads in flight per lane before their stores.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void window_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int32_t pieces_per_row,
-                           int32_t win, int32_t inverse, int64_t total_pieces, ImageTable tb) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= total_pieces) return;
-  const int p = static_cast<int>(i / pieces_per_row);
-  const int piece = static_cast<int>(i - static_cast<int64_t>(p) * pieces_per_row);
+                           int32_t win, int32_t inverse, int32_t n_rows, ImageTable tb) {
+  const int p = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  if (p >= n_rows) return;
+  const int lane = threadIdx.x & 63;
   const int img = image_of(tb, p);
   const int r = tb.start[img] + window_to_raster(p - tb.start[img], tb.gh[img], tb.gw[img], win);
   const int from = inverse ? p : r, to = inverse ? r : p;
-  dst[static_cast<int64_t>(to) * pieces_per_row + piece] = src[static_cast<int64_t>(from) * pieces_per_row + piece];
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* __restrict__ s = reinterpret_cast<const u32x4*>(src) + static_cast<int64_t>(from) * pieces_per_row;
+  u32x4* __restrict__ d = reinterpret_cast<u32x4*>(dst) + static_cast<int64_t>(to) * pieces_per_row;
+  // loads unconditional (lanes past the row end re-read its last piece) and fenced
+  // before the first store, so all four are in flight together; stores predicated
+  for (int64_t k0 = 0; k0 < pieces_per_row; k0 += 256) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = s[min(k0 + u * 64 + lane, static_cast<int64_t>(pieces_per_row) - 1)];
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (k0 + u * 64 + lane < pieces_per_row) d[k0 + u * 64 + lane] = v[u];
+  }
 }
-
-constexpr int kRopeHeadGroup = 4;  // heads per thread: angles computed once for them
 
 struct RopeArgs {
   void* x;
@@ -84,65 +96,80 @@ struct RopeArgs {
   int32_t H, d;
   int32_t win;         // 0: tokens in raster order; > 0: in window order of this window
   int32_t pieces;      // 16-byte pieces per head (d*elem/16)
-  int32_t groups;      // head groups per token: ceil(H / kRopeHeadGroup)
   float inv_freq[32];  // theta^(-4i/d), i < d/4
   ImageTable tb;
 };
 
-// One thread = one 16-byte piece (8 bf16 or 4 f32 values: whole pairs inside one half
-// of a head, since d/2 is a multiple of 8) of one token, for up to kRopeHeadGroup
-// heads: the angles depend on the token and the pair only, so they are computed once
-// and applied to each head of the group.  In place.
+// One wave = one token, in place.  The token's patch position is wave-uniform and
+// computed once; lane j < d/2 computes cos and sin of rotation pair j (pairs below d/4
+// rotate by the column, the rest by the row, frequency index j mod d/4), and every
+// 16-byte piece of the token's H*d values (8 bf16 or 4 f32: whole pairs of one half
+// of a head, as d/2 is a multiple of 8) takes its pairs' values from those lanes by
+// lane shuffles, made with every lane active before the bounds test.
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
-void rope2d_kernel(RopeArgs a, int64_t total_threads) {
+void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
   constexpr int kPer = 16 / sizeof(T);  // values per piece
   constexpr int kPairs = kPer / 2;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= total_threads) return;
-  const int per_token = a.pieces * a.groups;
-  const int t = static_cast<int>(i / per_token);
-  const int rem = static_cast<int>(i - static_cast<int64_t>(t) * per_token);
-  const int grp = rem / a.pieces, piece = rem % a.pieces;
+  const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
+  if (t >= n_tokens) return;
+  const int lane = threadIdx.x & 63;
   const int img = image_of(a.tb, t);
   const int p = t - a.tb.start[img];
   const int gw = a.tb.gw[img];
   const int r = a.win > 0 ? window_to_raster(p, a.tb.gh[img], gw, a.win) : p;
-  const int c0 = piece * kPer;          // first channel of the piece inside its head
-  const int half = a.d / 2;
-  const float pos = static_cast<float>(c0 < half ? r % gw + 1 : r / gw + 1);
-  const int i0 = (c0 % half) / 2;       // pair index of the piece's first pair
-  float cs[kPairs], sn[kPairs];
+  const int quarter = a.d / 4;  // pairs per half of a head
+  const float f_l = a.inv_freq[lane < 2 * quarter ? lane % quarter : 0];  // loaded before the data
+  float c_l = 1.0f, s_l = 0.0f;
+  T* row = static_cast<T*>(a.x) + static_cast<int64_t>(t) * a.ld;
+  const int total = a.H * a.pieces;
+  constexpr int kU = 4;  // pieces per lane loaded together
+  for (int j0 = 0; j0 < total; j0 += 64 * kU) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 raw[kU];
+    int off[kU], pcs[kU];
 #pragma unroll
-  for (int j = 0; j < kPairs; ++j) sincosf(pos * a.inv_freq[i0 + j], &sn[j], &cs[j]);
-  const int h0 = grp * kRopeHeadGroup, h1 = min(a.H, h0 + kRopeHeadGroup);
-  T* row = static_cast<T*>(a.x) + static_cast<int64_t>(t) * a.ld + c0;
-  uint4 raw[kRopeHeadGroup];
-#pragma unroll
-  for (int k = 0; k < kRopeHeadGroup; ++k)
-    if (h0 + k < h1) raw[k] = *reinterpret_cast<const uint4*>(row + static_cast<int64_t>(h0 + k) * a.d);
-#pragma unroll
-  for (int k = 0; k < kRopeHeadGroup; ++k) {
-    if (h0 + k >= h1) break;
-    uint32_t w[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float re = __uint_as_float(w[j] << 16), im = __uint_as_float(w[j] & 0xffff0000u);
-        const __bf16 a2 = static_cast<__bf16>(re * cs[j] - im * sn[j]);
-        const __bf16 b2 = static_cast<__bf16>(re * sn[j] + im * cs[j]);
-        w[j] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a2)) |
-               (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) << 16);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float re = __uint_as_float(w[2 * j]), im = __uint_as_float(w[2 * j + 1]);
-        w[2 * j] = __float_as_uint(re * cs[j] - im * sn[j]);
-        w[2 * j + 1] = __float_as_uint(re * sn[j] + im * cs[j]);
-      }
+    for (int u = 0; u < kU; ++u) {
+      const int j = min(j0 + u * 64 + lane, total - 1);  // past the end: re-read the last piece
+      const int head = j / a.pieces;
+      pcs[u] = j - head * a.pieces;
+      off[u] = head * a.d + pcs[u] * kPer;
+      raw[u] = *reinterpret_cast<const u32x4*>(row + off[u]);
     }
-    *reinterpret_cast<uint4*>(row + static_cast<int64_t>(h0 + k) * a.d) = uint4{w[0], w[1], w[2], w[3]};
+    if (j0 == 0 && lane < 2 * quarter) {  // the angles, while the first loads are in flight
+      const float pos = static_cast<float>(lane < quarter ? r % gw + 1 : r / gw + 1);
+      sincosf(pos * f_l, &s_l, &c_l);
+    }
+    asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]), "v"(raw[3]));
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float cs[kPairs], sn[kPairs];
+#pragma unroll
+      for (int k = 0; k < kPairs; ++k) {  // every lane active here
+        const int src = (pcs[u] * kPairs + k) & 63;
+        cs[k] = __shfl(c_l, src);
+        sn[k] = __shfl(s_l, src);
+      }
+      uint32_t w[4] = {raw[u][0], raw[u][1], raw[u][2], raw[u][3]};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float re = __uint_as_float(w[k] << 16), im = __uint_as_float(w[k] & 0xffff0000u);
+          const __bf16 a2 = static_cast<__bf16>(re * cs[k] - im * sn[k]);
+          const __bf16 b2 = static_cast<__bf16>(re * sn[k] + im * cs[k]);
+          w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a2)) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) << 16);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float re = __uint_as_float(w[2 * k]), im = __uint_as_float(w[2 * k + 1]);
+          w[2 * k] = __float_as_uint(re * cs[k] - im * sn[k]);
+          w[2 * k + 1] = __float_as_uint(re * sn[k] + im * cs[k]);
+        }
+      }
+      if (j0 + u * 64 + lane < total) *reinterpret_cast<u32x4*>(row + off[u]) = u32x4{w[0], w[1], w[2], w[3]};
+    }
   }
 }
 
