@@ -208,6 +208,35 @@ def test_decode_split_scales_and_reuse(torch):
     _check_ws(torch, "decode split reuse 2", [700, 1200], 32, 2, 128, 0, seed=925, ws=ws)
 
 
+def test_decode_split_across_launches(torch):
+    """More sequences than one launch holds: 150 one-token rows (and empty rows) go to
+    a launch of 120 sequences (240 pairs, unsplit) and one of 30 (60 pairs, split 4
+    ways), both through one workspace in stream order."""
+    rng = np.random.default_rng(941)
+    lk = rng.integers(1, 3000, size=150).tolist()
+    lq = [1] * 150
+    lq[7] = 0
+    lq[130] = 0
+    n, Hq, Hkv, d, W = 150, 32, 2, 128, 2048
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    nbytes = mg.mgattn_attention_kv_workspace(list(cq), list(ck), n, Hq, Hkv, d, W, wl.BF16)
+    assert nbytes > 0
+    say(f"decode split across launches: n={n} workspace={nbytes}")
+    q, qf = _arr(951, (int(cq[-1]), Hq * d), wl.BF16)
+    k, kf = _arr(952, (int(ck[-1]), Hkv * d), wl.BF16)
+    v, vf = _arr(953, (int(ck[-1]), Hkv * d), wl.BF16)
+    qd, kd, vd = (to_device(x, torch) for x in (q, k, v))
+    out = torch.full_like(qd, -777.0)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    mg.mgattn_attention_kv_ws(qd, kd, vd, out, Hq * d, Hkv * d, Hkv * d, Hq * d, list(cq), list(ck), n, Hq, Hkv, d,
+                              d ** -0.5, W, wl.BF16, ws, nbytes, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got = from_device(out, torch).reshape(int(cq[-1]), Hq, d)
+    want = G.attention_kv(qf, kf, vf, cq, ck, Hq, Hkv, d, d ** -0.5, W)
+    assert np.abs(got - want).max() <= BF16_TOL
+
+
 def test_decode_without_workspace_is_the_plain_entry(torch):
     """workspace_bytes = 0 runs exactly mgattn_attention_kv (bit for bit)."""
     lk = [4096] * 4
