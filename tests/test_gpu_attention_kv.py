@@ -80,6 +80,28 @@ def test_small_windows(torch, window):
     _check(torch, f"window{window}", [300, 1, 77], [300, 9, 600], 4, 1, 64, window, wl.BF16, seed=831)
 
 
+def test_window_wider_than_every_cache_is_no_window(torch):
+    """A window beyond every sequence's keys (up to 2^31 - 1) masks nothing: bit for bit
+    the plain causal call (window 0), prefill and cache rows alike."""
+    Hq, Hkv, d = 8, 2, 128
+    lq, lk = [300, 1, 77], [300, 9, 600]
+    cq = [0] + list(np.cumsum(lq))
+    ck = [0] + list(np.cumsum(lk))
+    q = to_device(_arr(961, (cq[-1], Hq * d), wl.BF16)[0], torch)
+    k = to_device(_arr(962, (ck[-1], Hkv * d), wl.BF16)[0], torch)
+    v = to_device(_arr(963, (ck[-1], Hkv * d), wl.BF16)[0], torch)
+    s = torch.cuda.current_stream()
+    outs = []
+    for window in (0, 600, 2 ** 31 - 1):
+        say(f"wide window {window}")
+        o = torch.empty_like(q)
+        mg.mgattn_attention_kv(q, k, v, o, Hq * d, Hkv * d, Hkv * d, Hq * d, cq, ck, 3, Hq, Hkv, d, 0.09, window,
+                               wl.BF16, s)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 @pytest.mark.parametrize("d,Hq,Hkv", [(64, 8, 8), (96, 16, 4), (128, 6, 3), (96, 3, 1)])
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
 def test_groupings_and_head_dims(torch, d, Hq, Hkv, dtype):

@@ -360,18 +360,45 @@ void attn_fwd_bf16(KernelArgs a) {
   // VALU phase j: online softmax of step j's scores into bf16 probabilities.  Keys
   // past the segment end and (causal) keys after the query get s = -inf, hence p = 0
   // (c is always positive).
+  // General instantiation: steps j_lo .. j_hi need no mask for any row of the wave
+  // (every key inside each row's window, at or before its position, before the segment
+  // end), and the per-lane limits are taken relative to the lane's first key of a step,
+  // so the loop keeps two step bounds and three lane values instead of the segment's
+  // scalars (which would not fit the SGPRs beside the DMA state).
+  const int pos_lo = off + qmin / G, pos_hi = off + (qmin + 31) / G;  // the wave's first and last positions
+  int j_lo = 0, j_hi = 0, lim_end = 0, lim_causal = 0, lim_window = 0;
+  if constexpr (kGeneral) {
+    j_lo = window > 0 ? max(0, (pos_hi - window + 1 - kb0 + SK - 1) / SK) : 0;
+    j_hi = (Lk - SK - kb0) >= 0 ? (Lk - SK - kb0) / SK : -1;
+    if (a.causal) j_hi = min(j_hi, (pos_lo - SK + 1 - kb0) >= 0 ? (pos_lo - SK + 1 - kb0) / SK : -1);
+    // (2^30 sentinels: key0 < 2^30 for any admitted segment, so the differences stay in
+    // range; a window wider than the keys masks nothing, as does a window of Lk)
+    lim_end = Lk - 4 * hf;                                                  // masked: key offset >= lim_end - key0
+    lim_causal = a.causal ? qpos - 4 * hf : (1 << 30);                      // masked: offset > lim_causal - key0
+    lim_window = window > 0 ? qpos - min(window, Lk) - 4 * hf : -(1 << 30);  // masked: offset <= lim_window - key0
+  }
   auto valu_phase = [&](int j) {
     if (kPrefetchK && j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
     const int key0 = kb0 + j * SK;
-    const int pos_lo = off + qmin / G, pos_hi = off + (qmin + 31) / G;  // the wave's first and last positions
-    if ((key0 + SK > Lk) || (a.causal && key0 + SK - 1 > pos_lo) || (window > 0 && key0 < pos_hi - window + 1)) {
+    if constexpr (kGeneral) {
+      if (j < j_lo || j > j_hi) {
+        const int d_end = lim_end - key0, d_causal = lim_causal - key0, d_window = lim_window - key0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kofs = b * 32 + acc_row(r, 0);  // key offset of register r from the lane's first key
+            if (kofs >= d_end || kofs > d_causal || kofs <= d_window) s[b][r] = -INFINITY;
+          }
+      }
+    } else if ((key0 + SK > Lk) || (a.causal && key0 + SK - 1 > pos_lo)) {
       const int pos = qpos;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + b * 32 + acc_row(r, hf);
-          if (key >= Lk || (a.causal && key > pos) || (window > 0 && key <= pos - window)) s[b][r] = -INFINITY;
+          if (key >= Lk || (a.causal && key > pos)) s[b][r] = -INFINITY;
         }
     }
     float mx = s[0][0];
