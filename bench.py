@@ -188,6 +188,47 @@ def token_path(torch, mg, wl, layers):
     return res
 
 
+def segment_sweep(torch, mg, wl, dev) -> int:
+    """Dense kernel on one 4096 x 16 x 96 input cut into equal segments of 256 .. 4096 tokens.
+
+    Every cut gives 256 workgroups (16 heads x 16 query tiles of 256), one per CU, each
+    running S/64 steps of 64 keys, so the launch time is a fixed cost plus S/64 times the
+    cost of one step; the least-squares line through the points separates the two."""
+    c = wl.tower_layer(3)
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (c.q, c.k, c.v))
+    out = torch.empty_like(q)
+    T, H, D = c.T, wl.HEADS, wl.HEAD_DIM
+    pts = []
+    for S in (256, 512, 1024, 2048, 4096):
+        cu = list(range(0, T + 1, S))
+        n = len(cu) - 1
+
+        def launch():
+            mg.mgattn_dense(q, k, v, out, cu, n, H, D, wl.SCALE, 0, mg.MGATTN_BF16, None)
+
+        for _ in range(3):
+            launch()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(50):
+                launch()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / 50)
+        us = min(ts)
+        flops = 4 * S * S * D * H * n
+        pts.append((S // 64, us))
+        print(f"segment {S:5d} x {n:2d}: {us:8.2f} us per launch (50 back to back, best of 5), "
+              f"{flops / us / 1e6:7.1f} TFLOP/s, {S // 64:2d} steps per workgroup", flush=True)
+    x = np.array([p[0] for p in pts], float)
+    y = np.array([p[1] for p in pts], float)
+    slope, icept = np.polyfit(x[1:], y[1:], 1)
+    print(f"fit over 512..4096: {icept:.2f} us fixed per launch + {slope:.3f} us per 64-key step", flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +240,9 @@ def main() -> int:
                     help="skip detail.token_path (profiling runs that count only the tower's launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--segment-sweep", action="store_true",
+                    help="print the attention kernel's time at 4096 tokens for segment lengths 256..4096 "
+                         "(fixed cost per launch vs cost per 64-key step) and exit; no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -214,6 +258,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.segment_sweep:
+        return segment_sweep(torch, mg, wl, dev)
     print(f"[bench] device {torch.cuda.get_device_name(0)}; generating 50 layers of seeded inputs", file=sys.stderr,
           flush=True)
 

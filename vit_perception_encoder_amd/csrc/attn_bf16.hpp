@@ -177,10 +177,11 @@ void attn_fwd_bf16(KernelArgs a) {
   constexpr int VDMA_W = (VDMA + TL::kWaves - 1) / TL::kWaves;
   constexpr float kRescaleLog2 = 8.0f;  // refresh the running max past 2^8 growth
   static_assert(TL::kQBlocks == 1, "one 32-query block per wave");
-  // K operands of the next QK product are read during the softmax phase, except at
-  // head_dim 128, where their 64 registers would spill: there they are read in the
-  // MFMA phase that uses them (the tile is resident by then).
-  constexpr bool kPrefetchK = D < 128;
+  // K operands of the next QK product are read during the softmax phase.  At
+  // head_dim 128 all of them (64 registers) would spill, so only the first half of
+  // the contraction's fragments is read there and the rest at the start of the MFMA
+  // phase that uses them; the QK product consumes the fragments in that order.
+  constexpr int kPreK = D < 128 ? KS : KS / 2;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
 
@@ -339,11 +340,11 @@ void attn_fwd_bf16(KernelArgs a) {
         }
       }
   };
-  auto read_k = [&](int j) {
+  auto read_k = [&](int j, int st0, int st1) {  // fragments st0 .. st1-1 of step j
     const __bf16* ks = step_buf(j);
     const int kb0 = step_b(j);
 #pragma unroll
-    for (int st = 0; st < KS; ++st)
+    for (int st = st0; st < st1; ++st)
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         kpre[st][b] = *reinterpret_cast<const bf16x8*>(ks + ((kb0 + b) * 32 + n) * KP + 16 * st + 8 * hf);
@@ -378,7 +379,7 @@ void attn_fwd_bf16(KernelArgs a) {
     lim_window = window > 0 ? qpos - min(window, Lk) - 4 * hf : -(1 << 30);  // masked: offset <= lim_window - key0
   }
   auto valu_phase = [&](int j) {
-    if (kPrefetchK && j + 1 < nsteps) read_k(j + 1);  // in flight while the softmax runs
+    if (j + 1 < nsteps) read_k(j + 1, 0, kPreK);  // in flight while the softmax runs
     const int key0 = kb0 + j * SK;
     if constexpr (kGeneral) {
       if (j < j_lo || j > j_hi) {
@@ -531,7 +532,7 @@ void attn_fwd_bf16(KernelArgs a) {
   if (wave < 4) {
     read_q();
     stage_begin(0);
-    read_k(0);
+    read_k(0, 0, KS);
     mfma_qk();
     stage_end(0);
     __syncthreads();
@@ -541,7 +542,7 @@ void attn_fwd_bf16(KernelArgs a) {
       stage_end(2 * j + 1);
       __syncthreads();
       stage_begin(2 * j + 2);
-      if (!kPrefetchK) read_k(j + 1);
+      if (kPreK < KS) read_k(j + 1, kPreK, KS);
       mfma_qk();
       mfma_pv(j);
       stage_end(2 * j + 2);
@@ -564,7 +565,7 @@ void attn_fwd_bf16(KernelArgs a) {
     __syncthreads();
     read_q();
     stage_begin(1);
-    read_k(0);
+    read_k(0, 0, KS);
     mfma_qk();
     stage_end(1);
     __syncthreads();
@@ -574,7 +575,7 @@ void attn_fwd_bf16(KernelArgs a) {
       stage_end(2 * j + 2);
       __syncthreads();
       stage_begin(2 * j + 3);
-      if (!kPrefetchK) read_k(j + 1);
+      if (kPreK < KS) read_k(j + 1, kPreK, KS);
       mfma_qk();
       mfma_pv(j);
       stage_end(2 * j + 3);
