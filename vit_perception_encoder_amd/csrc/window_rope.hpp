@@ -78,7 +78,9 @@ void window_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ ds
   const u32x4* __restrict__ s = reinterpret_cast<const u32x4*>(src) + static_cast<int64_t>(from) * pieces_per_row;
   u32x4* __restrict__ d = reinterpret_cast<u32x4*>(dst) + static_cast<int64_t>(to) * pieces_per_row;
   // loads unconditional (lanes past the row end re-read its last piece) and fenced
-  // before the first store, so all four are in flight together; stores predicated
+  // before the first store, so all four are in flight together; stores predicated and
+  // non-temporal (nothing in this launch reads them back, and dirty L2 lines would be
+  // written back at the kernel's end, delaying the next launch)
   for (int64_t k0 = 0; k0 < pieces_per_row; k0 += 256) {
     u32x4 v[4];
 #pragma unroll
@@ -86,7 +88,7 @@ void window_permute_kernel(const uint4* __restrict__ src, uint4* __restrict__ ds
     asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (k0 + u * 64 + lane < pieces_per_row) d[k0 + u * 64 + lane] = v[u];
+      if (k0 + u * 64 + lane < pieces_per_row) __builtin_nontemporal_store(v[u], d + k0 + u * 64 + lane);
   }
 }
 
