@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "../../include/mgattn.h"
@@ -128,18 +129,21 @@ int validate(const void* q, const void* k, const void* v, void* out, int64_t ldq
   return MGATTN_OK;
 }
 
-// gfx950 check, cached per device ordinal.
+// gfx950 check, cached per device ordinal (atomic entries: callers on several host
+// threads may race to fill one; they all store the same value).
 int device_ok() {
-  static int cache[64];  // 0 unknown, 1 yes, 2 no
+  static std::atomic<int> cache[64];  // 0 unknown, 1 yes, 2 no
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
-    cache[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    c = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(c, std::memory_order_relaxed);
   }
-  return cache[dev] == 1;
+  return c == 1;
 }
 
 template <typename Kern>
