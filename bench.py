@@ -138,15 +138,13 @@ def token_path(torch, mg, wl, layers):
         moved = 2 * T * row * 2  # read + write
         qkv3 = torch.randn(T, 3 * row, device=dev).to(torch.bfloat16)
 
-        def rope_qk():
-            for part in (0, 1):
-                mg.mgattn_rope2d(qkv3[:, part * row:(part + 1) * row], qkv3.stride(0), grids, 32, H, d, THETA,
-                                 mg.MGATTN_BF16, stream)
-        ms_r = time_launches(torch, rope_qk)
+        # q and k are adjacent in a merged qkv row: one call over their 2H heads
+        ms_r = time_launches(torch, lambda: mg.mgattn_rope2d(qkv3[:, :2 * row], qkv3.stride(0), grids, 32, 2 * H, d,
+                                                            THETA, mg.MGATTN_BF16, stream))
         rot = 2 * 2 * T * row * 2  # q and k, read + write
         res[f"window_gather_{name}"] = {"ms": ms_g, "bytes": moved, "gbs": moved / (ms_g * 1e-3) / 1e9,
                                         "frac_hbm": moved / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS}
-        res[f"rope2d_qk_{name}"] = {"ms": ms_r, "launches": 2, "bytes": rot, "gbs": rot / (ms_r * 1e-3) / 1e9,
+        res[f"rope2d_qk_{name}"] = {"ms": ms_r, "launches": 1, "bytes": rot, "gbs": rot / (ms_r * 1e-3) / 1e9,
                                     "frac_hbm": rot / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS}
     # text decoder attention (32 query / 2 key-value heads, head size 128, window 2048)
     Hq, Hkv, dt, W = 32, 2, 128, 2048

@@ -118,6 +118,25 @@ def test_rope2d_in_place_on_merged_qkv(torch):
                                                                    H, d, THETA), H, d, wl.BF16)
 
 
+def test_rope2d_q_and_k_in_one_call(torch):
+    """q and k are adjacent in a merged qkv row, so one call over 2H heads with the
+    merged row stride rotates both: the same result as the oracle on each part."""
+    H, d, grids, win = 16, 96, [(40, 40), (9, 33)], 32
+    T, row = _tokens(grids), H * d
+    say("rope2d on q and k of merged qkv in one call (2H heads)")
+    qkv = wl.f32_to_bf16_bits(wl.normal_f32(743, (T, 3 * row)))
+    buf = to_device(qkv, torch)
+    mg.mgattn_rope2d(buf[:, :2 * row], buf.stride(0), grids, win, 2 * H, d, THETA, wl.BF16,
+                     torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got = from_device(buf, torch)
+    ref = wl.bf16_bits_to_f32(qkv).astype(np.float64)
+    assert np.array_equal(got[:, 2 * row:], ref[:, 2 * row:]), "v columns were written"
+    for part in (0, 1):
+        _check_rope(got[:, part * row:(part + 1) * row], W.rope2d(ref[:, part * row:(part + 1) * row], grids, win,
+                                                                   H, d, THETA), H, d, wl.BF16)
+
+
 def _window_attention_rows(q, k, v, grids, win, scale, rows):
     """f64 attention of raster-order tokens `rows` over the keys of their window, with
     window membership computed from patch coordinates (no permutation)."""
