@@ -230,6 +230,16 @@ def test_decode_split_scales_and_reuse(torch):
     _check_ws(torch, "decode split reuse 2", [700, 1200], 32, 2, 128, 0, seed=925, ws=ws)
 
 
+def test_decode_split_repeated_calls_one_workspace(torch):
+    """Three calls in a row on one zero-filled workspace, which each call leaves holding
+    its partial results: every result matches the oracle and the first bit for bit."""
+    ws = torch.zeros((4 << 20,), dtype=torch.uint8, device="cuda")
+    first = _check_ws(torch, "decode split repeat 1", [2500] * 4, 32, 2, 128, 0, seed=931, ws=ws)
+    for i in (2, 3):
+        again = _check_ws(torch, f"decode split repeat {i}", [2500] * 4, 32, 2, 128, 0, seed=931, ws=ws)
+        assert np.array_equal(again, first)
+
+
 def test_decode_split_across_launches(torch):
     """More sequences than one launch holds: 150 one-token rows (and empty rows) go to
     a launch of 120 sequences (240 pairs, unsplit) and one of 30 (60 pairs, split 4
