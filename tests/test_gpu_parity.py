@@ -134,6 +134,29 @@ def test_scales(torch, scale):
     _full_check(torch, _rand_case(f"scale{scale}", [130, 270], H=2, scale=scale, seed=51))
 
 
+@pytest.mark.parametrize("case_seed", list(range(701, 713)))
+def test_random_segment_tables(torch, case_seed):
+    """Seeded random combinations of every parameter at once: 1-10 segments whose
+    lengths mix empty, single-token, tile-edge (63..65, 255..257) and ragged ones;
+    1-16 heads; head_dim 64/96/128; bf16 or f32; causal or not; scale of either sign.
+    Whole outputs against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(case_seed))
+    pool = [0, 1, 2, 31, 63, 64, 65, 255, 256, 257, 511, 777, 1024, 1300]
+    lens = [int(rng.choice(pool)) if rng.random() < 0.6 else int(rng.integers(1, 1400))
+            for _ in range(int(rng.integers(1, 11)))]
+    while sum(lens) > 2600:
+        lens.pop()
+    if sum(lens) == 0:
+        lens.append(97)
+    H = int(rng.choice([1, 2, 3, 5, 8, 16]))
+    d = int(rng.choice([64, 96, 128]))
+    dtype = wl.BF16 if rng.random() < 0.75 else wl.F32
+    causal = int(rng.random() < 0.4)
+    scale = float(rng.choice([-1.0, 1.0]) * rng.uniform(0.02, 0.25))
+    _full_check(torch, _rand_case(f"random{case_seed}", lens, H=H, d=d, dtype=dtype, causal=causal, scale=scale,
+                                  seed=case_seed))
+
+
 def test_many_segments_split_over_launches(torch):
     lens = np.random.Generator(np.random.PCG64(61)).integers(0, 90, size=300).tolist()
     case = _rand_case("300_segments", lens, H=2, seed=61)
