@@ -59,6 +59,29 @@ def _check(torch, name, lq, lk, Hq, Hkv, d, window, dtype, seed, scale=None):
     assert err.max() <= tol, f"max err {err.max():.3e} at (t,h,c)={worst}"
 
 
+@pytest.mark.parametrize("case_seed", list(range(1701, 1717)))
+def test_random_caches(torch, case_seed):
+    """Seeded random combinations: 1-6 sequences, each a prefill (as many queries as
+    keys), a one-token decode or new queries over a longer cache; 1-4 key/value heads of
+    1-16 query heads each; head_dim 64/96/128; no window or a random one; bf16 or f32;
+    scale of either sign.  Whole outputs against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(case_seed))
+    n = int(rng.integers(1, 7))
+    lk = [int(rng.choice([1, 2, 63, 64, 65, 255, 256, 257])) if rng.random() < 0.4 else int(rng.integers(1, 1200))
+          for _ in range(n)]
+    lq = []
+    for L in lk:
+        r = rng.random()
+        lq.append(L if r < 0.4 else (1 if r < 0.7 else int(rng.integers(0, L + 1))))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8, 16] if Hkv < 4 else [1, 2, 4]))
+    d = int(rng.choice([64, 96, 128]))
+    window = 0 if rng.random() < 0.4 else int(rng.integers(1, 1300))
+    dtype = wl.BF16 if rng.random() < 0.75 else wl.F32
+    scale = float(rng.choice([-1.0, 1.0]) * rng.uniform(0.02, 0.25))
+    _check(torch, f"random{case_seed}", lq, lk, Hq, Hkv, d, window, dtype, seed=case_seed, scale=scale)
+
+
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
 def test_text_decoder_prefill_longer_than_window(torch, dtype):
     _check(torch, "prefill", [2600], [2600], 32, 2, 128, 2048, dtype, seed=801)
