@@ -56,6 +56,43 @@ def test_window_permute_bit_exact(torch, grids, win, row_bytes):
     assert np.array_equal(back.cpu().numpy(), x)
 
 
+def _random_grids(rng, win):
+    """1-5 images with sides 1..80 (most not multiples of the window)."""
+    return [(int(rng.integers(1, 81)), int(rng.integers(1, 81))) for _ in range(int(rng.integers(1, 6)))], win
+
+
+@pytest.mark.parametrize("case_seed,win", [(2701, 1), (2702, 3), (2703, 8), (2704, 16), (2705, 32), (2706, 32)])
+def test_random_grids_permute_and_rope(torch, case_seed, win):
+    """Seeded random image batches: the gather into window order and back is bit exact,
+    and RoPE in window order (head_dim 64/96/128, bf16 or f32) matches the oracle."""
+    rng = np.random.Generator(np.random.PCG64(case_seed))
+    grids, win = _random_grids(rng, win)
+    T = _tokens(grids)
+    row_bytes = int(rng.choice([16, 48, 3072]))
+    say(f"random grids={grids} win={win} row_bytes={row_bytes}")
+    x = rng.integers(0, 256, size=(T, row_bytes), dtype=np.uint8)
+    src = torch.from_numpy(x).cuda()
+    dst = torch.zeros_like(src)
+    back = torch.zeros_like(src)
+    mg.mgattn_window_permute(src, dst, row_bytes, grids, win, 0, torch.cuda.current_stream())
+    mg.mgattn_window_permute(dst, back, row_bytes, grids, win, 1, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), W.to_window_order(x, grids, win))
+    assert np.array_equal(back.cpu().numpy(), x)
+    H, d = int(rng.choice([1, 4, 16])), int(rng.choice([64, 96, 128]))
+    dtype = wl.BF16 if rng.random() < 0.6 else wl.F32
+    xr = wl.normal_f32(case_seed, (T, H * d))
+    if dtype == wl.BF16:
+        xr = wl.f32_to_bf16_bits(xr)
+        xin = wl.bf16_bits_to_f32(xr)
+    else:
+        xin = xr
+    xd = to_device(xr, torch)
+    mg.mgattn_rope2d(xd, H * d, grids, win, H, d, THETA, dtype, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    _check_rope(from_device(xd, torch), W.rope2d(xin, grids, win, H, d, THETA), H, d, dtype)
+
+
 def _rope_bound(want_pairs_norm, dtype):
     angle = 129 * 2.0 ** -23 + 2e-7
     return want_pairs_norm * (angle + (2.0 ** -8 if dtype == wl.BF16 else 0.0)) + 1e-7
