@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -45,10 +46,19 @@ KERNEL_SOURCES = ["vit_perception_encoder_amd/csrc/attn_bf16.hpp", "vit_percepti
                   "vit_perception_encoder_amd/csrc/mgattn.hip"]
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed (string literals
+    of these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """sha256 of the attention kernel's sources, comments and layout ignored."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        h.update((ROOT / rel).read_bytes())
+        h.update(_code_only((ROOT / rel).read_text()).encode())
     return h.hexdigest()
 
 

@@ -25,10 +25,11 @@
 //     lane's 16 bytes land at M0 + 16*lane, no registers involved) into three LDS
 //     stages (two for head_dim 128), issued two phases before they are published.
 //     The K operands of the next QK product are read from LDS during the softmax
-//     phase, so the MFMA phase issues its QK MFMAs back to back.
-//     K rows are padded to 13 x 16 bytes (pitch 208 B: every 16-byte MFMA operand
-//     read is free of bank conflicts); the padding slot of a row receives a second
-//     copy of its last 16 bytes, so every DMA lane is active.
+//     phase (at head_dim 128 the first half of them; the rest at the start of the
+//     MFMA phase), so the MFMA phase issues its QK MFMAs back to back.
+//     K rows are padded by one 16-byte slot (D/8 + 1 slots: 208 B at head_dim 96;
+//     every 16-byte MFMA operand read is free of bank conflicts); the padding slot of a
+//     row receives a second copy of its last 16 bytes, so every DMA lane is active.
 //   * Softmax (per 64-key step) uses exp2 with scale*log2(e) folded into one FMA per
 //     score.  The running maximum is refreshed only when a step's maximum exceeds it
 //     by more than 2^8 in probability terms (decided per wave), so the O rescale is
