@@ -254,6 +254,41 @@ def segment_sweep(torch, mg, wl, dev) -> int:
     return 0
 
 
+def shape_sweep(torch, mg, dev) -> int:
+    """Dense kernel (bf16) at the tower's row width 1536 split as 24x64, 16x96 or 12x128
+    heads, T = 1024..16384 tokens, one segment or 1024-token windows; seeded N(0,1)
+    inputs, 30 back-to-back launches after a warm-up, best of 3."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    for d, H in ((64, 24), (96, 16), (128, 12)):
+        for T in (1024, 4096, 16384):
+            q, k, v = (torch.randn(T, H * d, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+            out = torch.empty_like(q)
+            for seg in ((T,) if T == 1024 else (T, 1024)):
+                cu = list(range(0, T + 1, seg))
+                n = len(cu) - 1
+
+                def launch():
+                    mg.mgattn_dense(q, k, v, out, cu, n, H, d, d ** -0.5, 0, mg.MGATTN_BF16, None)
+
+                for _ in range(10):
+                    launch()
+                best = float("inf")
+                for _ in range(3):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(30):
+                        launch()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    best = min(best, e0.elapsed_time(e1) * 1e3 / 30)
+                flops = 4.0 * seg * seg * d * H * n
+                print(f"d={d:3d} H={H:2d} T={T:5d} segments {n:2d} x {seg:5d}: {best:8.1f} us "
+                      f"{flops / best / 1e6:7.1f} TFLOP/s ({flops / best / 1e6 / PEAK_BF16_TFLOPS:.1%} of peak)",
+                      flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +300,9 @@ def main() -> int:
                     help="skip detail.token_path (profiling runs that count only the tower's launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="print the dense kernel's TFLOP/s for head_dim 64/96/128 (rows of 1536), 1024..16384 "
+                         "tokens, one segment or 1024-token windows, and exit; no JSON line")
     ap.add_argument("--segment-sweep", action="store_true",
                     help="print the attention kernel's time at 4096 tokens for segment lengths 256..4096 "
                          "(fixed cost per launch vs cost per 64-key step) and exit; no JSON line")
@@ -285,6 +323,8 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     if args.segment_sweep:
         return segment_sweep(torch, mg, wl, dev)
+    if args.shape_sweep:
+        return shape_sweep(torch, mg, dev)
     print(f"[bench] device {torch.cuda.get_device_name(0)}; generating 50 layers of seeded inputs", file=sys.stderr,
           flush=True)
 
