@@ -122,6 +122,32 @@ def time_launches(torch, fn, reps: int = 30, warm: int = 10) -> float:
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
+def config_times(torch, mg, wl):
+    """Each parity workload timed on its own (events around each launch, median): the
+    f32 256-token segment, the 1024-token full layer, the 4 x 1024 window layer, and the
+    ragged batches' full and window layers (17,408 and 16,384 tokens)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    cases = [wl.config_tiny(), wl.config_full448(), wl.config_window896()]
+    for which in ("5a", "5b"):
+        qkv = wl.ragged_inputs(which)
+        cases += [wl.ragged_case(which, "full", qkv), wl.ragged_case(which, "window", qkv)]
+    res = {}
+    for c in cases:
+        if c.dtype == wl.BF16:
+            q, k, v = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev) for x in (c.q, c.k, c.v))
+        else:
+            q, k, v = (torch.from_numpy(x).to(dev) for x in (c.q, c.k, c.v))
+        out = torch.empty_like(q)
+        cu = [int(x) for x in c.cu_seqlens]
+        ms = time_launches(torch, lambda: mg.mgattn_dense(q, k, v, out, cu, c.n_seg, c.H, c.d, c.scale, c.causal,
+                                                          c.dtype, stream))
+        fl = c.flops()
+        res[c.name] = {"ms": ms, "tokens": c.T, "segments": c.n_seg, "dtype": "bf16" if c.dtype == wl.BF16 else "f32",
+                       "tflops": fl / (ms * 1e-3) / 1e12, "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    return res
+
+
 def token_path(torch, mg, wl, layers):
     """The other entry points on the same shapes: the 4096-token full layer read from a
     merged [T, 3*H*d] qkv buffer, and the HBM-bound token-order kernels (window gather
@@ -411,6 +437,7 @@ def main() -> int:
     print("[bench] timing the other entry points (merged qkv, window gather, 2D RoPE, text decoder)", file=sys.stderr,
           flush=True)
     token = None if args.no_token_path else token_path(torch, mg, wl, layers)
+    configs = None if args.no_token_path else config_times(torch, mg, wl)
 
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -466,6 +493,7 @@ def main() -> int:
             "wall_s_timed_region": wall,
             "oracle_parity_full_layers_max_abs_err": parity,
             "token_path": token,
+            "configs": configs,
             "kernel_source_sha256": kernel_source_hash(),
         },
     }
