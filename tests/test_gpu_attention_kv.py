@@ -263,6 +263,51 @@ def test_decode_split_repeated_calls_one_workspace(torch):
         assert np.array_equal(again, first)
 
 
+def test_decode_split_graph_capture_replays_match_eager(torch):
+    """One-token decoding with a workspace (decode kernel + merge kernel, no allocation,
+    no memset) captured into a HIP graph replays to the eager result bit for bit, with
+    unrelated eager work and synchronisations between the replays."""
+    n, Hq, Hkv, d, W = 8, 32, 2, 128, 2048
+    lk = [3000, 17, 900, 2048, 64, 4000, 1, 700]
+    cq = list(range(n + 1))
+    ck = [int(x) for x in np.concatenate([[0], np.cumsum(lk)])]
+    nbytes = mg.mgattn_attention_kv_workspace(cq, ck, n, Hq, Hkv, d, W, wl.BF16)
+    assert nbytes > 0
+    q, _ = _arr(961, (n, Hq * d), wl.BF16)
+    k, _ = _arr(962, (ck[-1], Hkv * d), wl.BF16)
+    v, _ = _arr(963, (ck[-1], Hkv * d), wl.BF16)
+    qd, kd, vd = (to_device(x, torch) for x in (q, k, v))
+    out = torch.zeros_like(qd)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+
+    def call(stream):
+        mg.mgattn_attention_kv_ws(qd, kd, vd, out, Hq * d, Hkv * d, Hkv * d, Hq * d, cq, ck, n, Hq, Hkv, d,
+                                  d ** -0.5, W, wl.BF16, ws, nbytes, stream)
+
+    call(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = from_device(out, torch)
+    say("decode split graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream())
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(out, torch), want), f"replay {rep}"
+        junk.mul_(1.0001)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_decode_split_across_launches(torch):
     """More sequences than one launch holds: 150 one-token rows (and empty rows) go to
     a launch of 120 sequences (240 pairs, unsplit) and one of 30 (60 pairs, split 4
