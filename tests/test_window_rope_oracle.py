@@ -141,6 +141,55 @@ def pin_width_first_axis_separation(w):
     assert np.abs(y[0, 3, :, D_ // 2:] - y[4, 3, :, D_ // 2:]).max() > 1e-3
 
 
+def roformer_1d(x, m, base=10000.0):
+    """1D rotary position embedding as RoFormer defines it (Su et al., 2021, "RoFormer:
+    Enhanced Transformer with Rotary Position Embedding", section 3.4.2, the
+    element-wise form of the rotary matrix product): for a vector x of even length n
+    at position m, with theta_i = base^(-2(i-1)/n) for i = 1 .. n/2,
+        R x = x * (cos m theta_1, cos m theta_1, cos m theta_2, cos m theta_2, ...)
+            + (-x_2, x_1, -x_4, x_3, ...) * (sin m theta_1, sin m theta_1, ...).
+    RoFormer rotates ADJACENT channel pairs (x_1, x_2), (x_3, x_4), ... (1-based); the
+    tower's reading is the same adjacent pairing (not the split-halves pairing of
+    x_i with x_(i+n/2)).  Written independently of the oracle: x is [..., n], m is
+    broadcast against x's leading axes."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    i = np.arange(1, n // 2 + 1, dtype=np.float64)
+    theta = base ** (-2.0 * (i - 1.0) / n)
+    ang = np.asarray(m, dtype=np.float64)[..., None] * np.repeat(theta, 2)
+    swapped = np.empty_like(x)
+    swapped[..., 0::2] = -x[..., 1::2]
+    swapped[..., 1::2] = x[..., 0::2]
+    return x * np.cos(ang) + swapped * np.sin(ang)
+
+
+def pin_roformer_per_axis(w):
+    """Width-first 2D RoPE = RoFormer's 1D RoPE applied per axis on half the channels:
+    channels [0, d/2) of every head are RoFormer-rotated (dimension n = d/2) at
+    position column + 1, channels [d/2, d) at row + 1.  So a 1 x W grid's width half is
+    exactly the 1D rotation at x + 1, and an H x 1 grid's height half the 1D rotation
+    at y + 1.  Pins the frequency schedule, the pairing, the sign and the 1-based
+    positions against a published definition."""
+    rng = np.random.default_rng(17)
+    for gh, gw in ((1, 11), (9, 1), (5, 7)):
+        T = gh * gw
+        x = rng.standard_normal((T, H_ * D_))
+        y = _rope(w, x, [(gh, gw)]).reshape(T, H_, D_)
+        xs = x.reshape(T, H_, D_)
+        rows = np.repeat(np.arange(gh), gw)[:, None] * np.ones((1, H_))
+        cols = np.tile(np.arange(gw), gh)[:, None] * np.ones((1, H_))
+        want_w = roformer_1d(xs[:, :, :D_ // 2], cols + 1)
+        want_h = roformer_1d(xs[:, :, D_ // 2:], rows + 1)
+        assert np.abs(y[:, :, :D_ // 2] - want_w).max() < 1e-12
+        assert np.abs(y[:, :, D_ // 2:] - want_h).max() < 1e-12
+    # also at the tower's head size (96 channels: 24 frequencies per axis)
+    x = rng.standard_normal((6, 96))
+    y = w.rope2d(x, [(2, 3)], 0, 1, 96, 10000.0)
+    r, c = np.repeat(np.arange(2), 3), np.tile(np.arange(3), 2)
+    assert np.abs(y[:, :48] - roformer_1d(x[:, :48], c + 1)).max() < 1e-12
+    assert np.abs(y[:, 48:] - roformer_1d(x[:, 48:], r + 1)).max() < 1e-12
+
+
 def pin_relative_position(w):
     """<R(p1) q, R(p2) k> is unchanged when both patches move by the same offset."""
     rng = np.random.default_rng(11)
@@ -165,7 +214,7 @@ def pin_window_order_positions(w):
 
 PINS = [pin_golden_5x7, pin_fixture_segment_counts, pin_segments_are_clipped_blocks, pin_identity_cases,
         pin_round_trip, pin_rotation_preserves_pair_norms, pin_angles_closed_form,
-        pin_width_first_axis_separation, pin_relative_position, pin_window_order_positions]
+        pin_width_first_axis_separation, pin_relative_position, pin_window_order_positions, pin_roformer_per_axis]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -210,3 +259,30 @@ def test_mutant_fails_a_pin(name, old, new):
         except Exception:  # any failure, assertion or error, counts as caught
             failed.append(pin.__name__)
     assert failed, f"mutant '{name}' passes every pin"
+
+
+def test_roformer_reference_itself():
+    """The RoFormer function is checked on its own against the 2x2 rotation it
+    stands for: pair i of a vector at position m turns by m * base^(-2(i-1)/n), and
+    the first pair (theta_1 = 1) by exactly m radians."""
+    x = np.zeros(8)
+    x[0] = 1.0
+    y = roformer_1d(x, 0.5)
+    assert abs(y[0] - math.cos(0.5)) < 1e-15 and abs(y[1] - math.sin(0.5)) < 1e-15
+    x = np.zeros(8)
+    x[6] = 1.0  # pair 4: theta_4 = 10000^(-6/8)
+    y = roformer_1d(x, 3.0)
+    ang = 3.0 * 10000.0 ** (-0.75)
+    assert abs(y[6] - math.cos(ang)) < 1e-15 and abs(y[7] - math.sin(ang)) < 1e-15
+
+
+@pytest.mark.parametrize("name", ["frequency exponent", "0-based positions", "height first", "sign of the sine term",
+                                  "reverse rotation"])
+def test_roformer_pin_alone_catches(name):
+    """The RoPE mutants are caught by the RoFormer pin on its own, not only by pins
+    that restate the oracle's formula."""
+    old, new = next((m[1], m[2]) for m in MUTANTS if m[0] == name)
+    mod = types.ModuleType(f"mutant_{name}")
+    exec(compile(SRC.replace(old, new, 1), f"<mutant {name}>", "exec"), mod.__dict__)
+    with pytest.raises(AssertionError):
+        pin_roformer_per_axis(mod)

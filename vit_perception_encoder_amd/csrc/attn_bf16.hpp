@@ -127,6 +127,10 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // m0 + 16*l.  Written as asm (no output registers; the address is read at issue) so
 // that the compiler does not order later LDS reads behind it: the one wait for the
 // DMA is the explicit vmcnt(0) before the barrier that publishes the tile.
+// M0 is not named as clobbered: LLVM reserves M0 and does not honour a clobber of a
+// reserved register.  These kernels make no other use of M0 (no LDS-DMA builtin,
+// interpolation, message or indexed lane access), which a host test checks on the
+// generated gfx950 assembly: every M0 write is the one inside these asm statements.
 __device__ inline void dma16(const void* g, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(g) : "memory");
 }

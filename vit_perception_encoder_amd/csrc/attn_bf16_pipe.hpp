@@ -1,0 +1,450 @@
+// Dense segmented attention, bf16 inputs, f32 accumulation, gfx950: the
+// software-pipelined main loop.
+//
+// Same operation as attn_fwd_bf16<D, false> (vllm.cpp issue #1545, sections "Why this
+// one is bad" and "The fix": every cu_seqlens segment attended on its own, online
+// softmax as in the flash rung of PR #1579, "Numerics, both halves"), same tile
+// (8 waves, 256 queries, 32 per wave; S^T = K Q^T and O^T = V^T P^T on
+// v_mfma_f32_32x32x16_bf16; K/V tiles of 128 keys in three LDS stages filled by LDS
+// DMA), but a different way of keeping the matrix core fed.
+//
+// On gfx950 one wave issues a VALU instruction at best every ~7 cycles, while the
+// SIMD accepts one from another wave in between; transcendentals take about 2.7
+// times the issue cost of an FMA.  So the softmax of a 64-key step (~120 VALU
+// instructions per wave, 32 of them v_exp_f32) cannot hide behind the other wave's
+// 24 MFMAs when one wave runs it alone.  Here every wave runs, per iteration j,
+//     PV(j-1)  --  O^T += V^T P(j-1)^T   (12 MFMAs at head_dim 96)
+//     QK(j+1)  --  S(j+1)^T = K Q^T      (12 MFMAs)
+//     SM(j)    --  online softmax of S(j) into P(j)
+// as one instruction stream: MFMA slot k is followed by the LDS operand reads of a
+// later slot and by a slice of the softmax, with a scheduling fence after each slot
+// so the compiler keeps that interleave.  Both waves of a SIMD do the same, so the
+// matrix core always has an MFMA waiting while the two VALU streams share the rest.
+// S and P are double-buffered (the MFMAs write S(j+1) and read P(j-1) while the
+// softmax reads S(j) and writes P(j)).
+//
+// LDS: K of step s is read in iteration s-1, V of step s in iteration s+1, so tile t
+// (steps 2t, 2t+1) is live in iterations 2t-1 .. 2t+2.  One barrier per tile, at the
+// start of odd iteration 2t+1: each wave first waits for its own DMA of tile t+1
+// (issued two iterations earlier), and after the barrier tile t-1's stage (last read
+// in iteration 2t) receives tile t+2.  The Q tile arrives by DMA in the third stage
+// before tile 2 does.
+//
+// Rescaling is lazy (the running maximum moves only when a row's maximum grows by more
+// than 2^8 in probability terms, decided per wave) and branch-free inside the loop:
+// the row sum takes the factor at once; O, which the same iteration's PV MFMAs still
+// accumulate into, takes it at the start of the next iteration, before PV(j).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "attn_bf16.hpp"
+#include "plan.hpp"
+
+namespace mgattn {
+
+template <int... K, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, K...>, F&& f) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+// f(integral_constant<int, k>) for k = 0 .. N-1, in order, k a constant expression.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, static_cast<F&&>(f));
+}
+
+// Scheduling fence: the compiler moves no instruction across it.
+#define MGATTN_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <int D>
+struct PipeTile {
+  using T = Bf16Tile<D>;
+  static constexpr int kNB = T::kStepKeys / 32;      // 32-key blocks per step
+  static constexpr int kKS = D / 16;                 // QK k-steps
+  static constexpr int kCT = D / 32;                 // 32-channel output tiles
+  static constexpr int kNPV = kNB * 2 * kCT;         // PV MFMAs per iteration
+  static constexpr int kNQK = kKS * kNB;             // QK MFMAs per iteration
+  static constexpr int kNSlot = kNPV + kNQK;
+  static constexpr int kDV = 2;                      // V^T read distance (slots)
+  static constexpr int kDK = 3;                      // K read distance (slots)
+  // Slots 0 .. kNPV-1: PV MFMA i = (32-key block b, 16-key half h2, channel tile ct),
+  // block-major, so block 0 of P(j-1) is dead after slot kNPV/2 - 1.
+  static constexpr int pv_b(int i) { return i / (2 * kCT); }
+  static constexpr int pv_h(int i) { return (i / kCT) % 2; }
+  static constexpr int pv_c(int i) { return i % kCT; }
+  // Slots kNPV ..: QK MFMA i = (block b, k-step st), block-major, so S(j+1) block 0
+  // overwrites S(j) block 0 only after the softmax has read it (slot kNPV on), and
+  // block 1 from slot kNPV + kKS on.
+  static constexpr int qk_b(int i) { return i / kKS; }
+  static constexpr int qk_s(int i) { return i % kKS; }
+  // Softmax slices: slots 0..3 the row maxima, slot 4 the running maximum; score pair
+  // u (of the lane's 16: block u/8) is exponentiated in slot exp_slot(u) and converted
+  // to bf16 and summed one slot later; the row sum takes the step in slot kLSlot.
+  // Block 0's pairs end before slot kNPV and block 1's before kNPV + kKS; the
+  // conversions of block 0 start at slot kNPV/2, after PV(j-1) has read P block 0.
+  static constexpr int exp_slot(int u) {
+    constexpr int tbl[16] = {5, 6, 7, 8, 9, 10, 11, 11, 12, 13, 13, 14, 15, 16, 16, 17};
+    return tbl[u];
+  }
+  static constexpr int kLSlot = 19;
+  static_assert(D == 96, "the slot plan is laid out for head_dim 96 (12 PV + 12 QK MFMAs)");
+  static_assert(kNPV == 12 && kKS == 6 && kNSlot == 24, "slot plan");
+  static_assert(T::kStages == 3, "the pipelined loop needs three LDS stages");
+  static_assert(T::kBlockN == 2 * T::kStepKeys, "two softmax steps per LDS tile");
+  static_assert(kNB == 2, "the softmax slices assume two 32-key blocks per step");
+  static_assert(kNPV >= kDK, "K reads start inside the PV slots");
+};
+
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16_pipe(KernelArgs a) {
+  using TL = Bf16Tile<D>;
+  using PT = PipeTile<D>;
+  constexpr int BM = TL::kBlockM, BN = TL::kBlockN;
+  constexpr int SK = TL::kStepKeys;
+  constexpr int NB = PT::kNB, KS = PT::kKS, CT = PT::kCT;
+  constexpr int NPV = PT::kNPV, NQK = PT::kNQK, NSLOT = PT::kNSlot;
+  constexpr int DV = PT::kDV, DK = PT::kDK;
+  constexpr int NSTEP = BN / SK;
+  constexpr int KP = TL::kKPitch, VP = TL::kVPitch, KSL = TL::kKSlots;
+  constexpr int KDMA = TL::kKDma, VDMA = TL::kVDma;
+  constexpr int KDMA_W = (KDMA + TL::kWaves - 1) / TL::kWaves;
+  constexpr int VDMA_W = (VDMA + TL::kWaves - 1) / TL::kWaves;
+  constexpr float kRescaleLog2 = 8.0f;
+
+  __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
+
+  const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
+  if (!tile.valid) return;
+  const int L = a.table.len[tile.slot];  // tokens of the segment (queries = keys)
+  const int q0 = tile.q0;
+  const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const __bf16* __restrict__ qg = static_cast<const __bf16*>(a.q) + t0 * a.ldq + hoff;
+  const __bf16* __restrict__ kg = static_cast<const __bf16*>(a.k) + t0 * a.ldk + hoff;
+  const __bf16* __restrict__ vg = static_cast<const __bf16*>(a.v) + t0 * a.ldv + hoff;
+  __bf16* __restrict__ og = static_cast<__bf16*>(a.o) + t0 * a.ldo + hoff;
+  const int ldk = a.ldk, ldv = a.ldv;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const float c = a.c;
+  const int qr = q0 + wave * 32 + n;  // this lane's query (relative to the segment)
+  const int qmin = q0 + wave * 32;    // the wave's first query
+
+  // keys this q-tile needs: all of the segment, or (causal) up to its last query
+  const int kend = a.causal ? min(L, q0 + BM) : L;
+  const int ntiles = (kend + BN - 1) / BN;
+  const int nsteps = (kend + SK - 1) / SK;
+
+  // ---- LDS DMA plan (as in attn_fwd_bf16): DMA instruction i of a tile fills 64
+  // consecutive 16-byte slots; wave w issues instructions w, w+8, ...  K slot s is row
+  // s/KSL, piece s%KSL (the padding piece D/8 repeats piece D/8-1); V slot s is row
+  // s/(D/8), piece s%(D/8).  Rows past the segment end are clamped to its last row.
+  auto k_row = [&](int u) { return ((wave + TL::kWaves * u) * 64 + lane) / KSL; };
+  auto k_off = [&](int u) { return min(((wave + TL::kWaves * u) * 64 + lane) % KSL, D / 8 - 1) * 8; };
+  auto v_row = [&](int u) { return ((wave + TL::kWaves * u) * 64 + lane) / (D / 8); };
+  auto v_off = [&](int u) { return (((wave + TL::kWaves * u) * 64 + lane) % (D / 8)) * 8; };
+  uint32_t k_boff[KDMA_W], v_boff[VDMA_W];
+#pragma unroll
+  for (int u = 0; u < KDMA_W; ++u)
+    k_boff[u] = (static_cast<uint32_t>(k_row(u)) * static_cast<uint32_t>(ldk) + k_off(u)) * 2u;
+#pragma unroll
+  for (int u = 0; u < VDMA_W; ++u)
+    v_boff[u] = (static_cast<uint32_t>(v_row(u)) * static_cast<uint32_t>(ldv) + v_off(u)) * 2u;
+  auto issue_tile = [&](int t, int part) {  // part: 1 = K, 2 = V, 3 = both
+    const int kt0 = t * BN;
+    const int last = L - 1 - kt0;
+    const __bf16* kb = kg + static_cast<size_t>(kt0) * ldk;
+    const __bf16* vb = vg + static_cast<size_t>(kt0) * ldv;
+    __bf16* kl = lds + (t % TL::kStages) * TL::kStageElems;
+    __bf16* vl = kl + TL::kKElems;
+    if (last >= BN - 1) {
+#pragma unroll
+      for (int u = 0; u < KDMA_W; ++u) {
+        const int i = wave + TL::kWaves * u;
+        if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA))
+          dma16s(kb, k_boff[u], __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
+      }
+#pragma unroll
+      for (int u = 0; u < VDMA_W; ++u) {
+        const int i = wave + TL::kWaves * u;
+        if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
+          dma16s(vb, v_boff[u], __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
+      }
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < KDMA_W; ++u) {
+      const int i = wave + TL::kWaves * u;
+      if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA))
+        dma16(kb + static_cast<size_t>(min(k_row(u), last)) * ldk + k_off(u),
+              __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
+    }
+#pragma unroll
+    for (int u = 0; u < VDMA_W; ++u) {
+      const int i = wave + TL::kWaves * u;
+      if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
+        dma16(vb + static_cast<size_t>(min(v_row(u), last)) * ldv + v_off(u),
+              __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
+    }
+  };
+  const int my_kdma = KDMA / TL::kWaves + (wave < KDMA % TL::kWaves ? 1 : 0);
+  const int my_vdma = VDMA / TL::kWaves + (wave < VDMA % TL::kWaves ? 1 : 0);
+
+  // ---- prologue: Q tile (to the third stage), tiles 0 and 1.  Q rows and K of tile
+  // 0 are waited for before the first barrier; V of tile 0 and tile 1 at the barrier
+  // of iteration 1.
+  constexpr int QDMA = BM * D / 8 / 64;
+  constexpr int QDMA_W = QDMA / TL::kWaves;
+  static_assert(QDMA % TL::kWaves == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  __bf16* ql = lds + (TL::kStages - 1) * TL::kStageElems;
+#pragma unroll
+  for (int u = 0; u < QDMA_W; ++u) {
+    const int i = wave + TL::kWaves * u;
+    const int slot = i * 64 + lane;
+    const int row = min(q0 + slot / (D / 8), L - 1);
+    dma16(qg + static_cast<size_t>(row) * a.ldq + (slot % (D / 8)) * 8,
+          __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
+  }
+  issue_tile(0, 1);
+  issue_tile(0, 2);
+  if (ntiles > 1) issue_tile(1, 3);
+  dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + my_vdma : 0));
+  __syncthreads();
+
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(ql + (wave * 32 + n) * D + 16 * s + 8 * hf);
+  if (qr >= L) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = bf16x8{};
+  }
+  if (a.qsign != 1) {
+    const __bf16 sg = static_cast<__bf16>(static_cast<float>(a.qsign));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = qf[s] * sg;
+  }
+
+  // ---- running state
+  f32x16 o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x16{};
+  float m_run = 0.0f, l_run = 0.0f, alpha = 1.0f;
+  int resc = 0;  // O waits for the factor alpha (wave-uniform)
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  f32x16 s[NB];       // S(j) until the softmax has read it, then S(j+1)
+  bf16x8 p[NB][2];    // P(j-1) until PV(j-1) has read it, then P(j)
+
+  auto stage_of = [&](int step) { return lds + ((step / NSTEP) % TL::kStages) * TL::kStageElems; };
+  // V^T transpose-read lane addressing (see attn_bf16.hpp)
+  const int tr_row = ((lane & 15) >> 2) + 4 * hf;
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // V^T operand of PV MFMA i for step js
+  auto read_v = [&](const __bf16* vt, int i) {
+    const __bf16* vrow = vt + ((PT::pv_b(i)) * 32 + PT::pv_h(i) * 16 + tr_row) * VP + tr_col + PT::pv_c(i) * 32;
+    const bf16x4 lo = ds_read_tr(vrow);
+    const bf16x4 hi = ds_read_tr(vrow + 8 * VP);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto read_k = [&](const __bf16* ks, int i) {
+    return *reinterpret_cast<const bf16x8*>(ks + (PT::qk_b(i) * 32 + n) * KP + 16 * PT::qk_s(i) + 8 * hf);
+  };
+
+  // Scores of step j past the segment end or (causal) after the query: -inf.
+  auto mask = [&](int j) {
+    const int key0 = j * SK;
+    if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + b * 32 + acc_row(r, hf);
+          if (key >= L || (a.causal && key > qr)) s[b][r] = -INFINITY;
+        }
+    }
+  };
+
+  // One iteration.  HAS_PV: PV(j-1); HAS_QK: QK(j+1); HAS_SM: the softmax of step j;
+  // FIRST: the first softmax step (sets the running maximum).
+  auto iteration = [&](int j, auto has_pv, auto has_qk, auto has_sm, auto first) {
+    constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value;
+    constexpr bool SM = decltype(has_sm)::value, FIRST = decltype(first)::value;
+    if constexpr (PV) {
+      if (resc) {  // the factor decided in the previous iteration, before PV(j-1) adds in
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+      }
+    }
+    if constexpr (SM) mask(j);
+    const __bf16* vt = PV ? stage_of(j - 1) + TL::kKElems + ((j - 1) % NSTEP) * NB * 32 * VP : lds;
+    const __bf16* ks = QK ? stage_of(j + 1) + ((j + 1) % NSTEP) * NB * 32 * KP : lds;
+    bf16x8 vf[NPV];
+    bf16x8 kf[NQK];
+    if constexpr (PV) {
+      static_for<DV>([&](auto ic) { vf[decltype(ic)::value] = read_v(vt, decltype(ic)::value); });
+    }
+    float ma = 0.0f, mb = 0.0f, mc = 0.0f, lsum = 0.0f;
+    float px[16][2];  // probabilities of a score pair, between its exp and its conversion
+    MGATTN_FENCE();
+    static_for<NSLOT>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      // -- the MFMA of slot k
+      if constexpr (k < NPV) {
+        if constexpr (PV)
+          o[PT::pv_c(k)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k], p[PT::pv_b(k)][PT::pv_h(k)], o[PT::pv_c(k)],
+                                                                   0, 0, 0);
+      } else {
+        constexpr int i = k - NPV;
+        if constexpr (QK) {
+          if constexpr (PT::qk_s(i) == 0)
+            s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0], f32x16{}, 0, 0, 0);
+          else
+            s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[PT::qk_s(i)], s[PT::qk_b(i)], 0, 0, 0);
+        }
+      }
+      // -- operand reads of later slots
+      if constexpr (PV && k + DV < NPV) vf[k + DV] = read_v(vt, k + DV);
+      if constexpr (QK && k + DK >= NPV && k + DK < NSLOT) kf[k + DK - NPV] = read_k(ks, k + DK - NPV);
+      // -- the softmax slice of slot k
+      if constexpr (SM) {
+        // slots 0..3: row maximum, two chains of max3 over the 16 scores of each block
+        if constexpr (k < 4) {
+          constexpr int r0 = 4 * k;
+          if constexpr (k == 0) {
+            ma = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+            mb = fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]));
+          } else {
+            ma = fmaxf(fmaxf(ma, s[0][r0]), fmaxf(s[0][r0 + 1], fmaxf(s[0][r0 + 2], s[0][r0 + 3])));
+            mb = fmaxf(fmaxf(mb, s[1][r0]), fmaxf(s[1][r0 + 1], fmaxf(s[1][r0 + 2], s[1][r0 + 3])));
+          }
+        }
+        if constexpr (k == 4) {
+          // a step with no visible key for some rows (causal) has maximum -inf; the
+          // floor keeps the reference finite (those rows get p = 0 and take alpha = 0
+          // at the first step with keys)
+          const float m_blk = fmaxf(half_swap_max(fmaxf(ma, mb)), -1.0e30f);
+          if constexpr (FIRST) {
+            m_run = m_blk;
+          } else {
+            const bool grow = __builtin_amdgcn_ballot_w64((m_blk - m_run) * c > kRescaleLog2) != 0;
+            const float m_new = grow ? fmaxf(m_run, m_blk) : m_run;
+            alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+            resc = grow;
+            m_run = m_new;
+          }
+          mc = m_run * c;
+        }
+        // probabilities, pair by pair: p = exp2(s*c - m*c), converted to bf16 (RNE)
+        // one slot later and added to the row sum
+        static_for<16>([&](auto uc) {
+          constexpr int u = decltype(uc)::value;
+          constexpr int b = u / 8, h2 = (u / 4) % 2, e = 2 * (u % 4);
+          if constexpr (PT::exp_slot(u) + 1 == k) {
+            const bf16x2 pr = {static_cast<__bf16>(px[u][0]), static_cast<__bf16>(px[u][1])};
+            p[b][h2][e] = pr[0];
+            p[b][h2][e + 1] = pr[1];
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+          }
+          if constexpr (PT::exp_slot(u) == k) {
+            px[u][0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e], c, -mc));
+            px[u][1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e + 1], c, -mc));
+          }
+        });
+        if constexpr (k == PT::kLSlot) {
+          if constexpr (FIRST) l_run = lsum;
+          else l_run = __builtin_fmaf(l_run, alpha, lsum);
+        }
+      }
+      MGATTN_FENCE();
+    });
+    if constexpr (!SM) resc = 0;
+  };
+
+  auto tile_sync = [&](int j) {  // start of odd iteration j = 2t+1
+    const int t = j >> 1;
+    dma_wait();  // this wave's DMA of tile t+1
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < ntiles) issue_tile(t + 2, 3);
+  };
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // ---- S(0), then iteration 0 (no PV)
+  {
+    const __bf16* ks = stage_of(0);
+    static_for<NQK>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const bf16x8 kf = read_k(ks, i);
+      if constexpr (PT::qk_s(i) == 0)
+        s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], f32x16{}, 0, 0, 0);
+      else
+        s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[PT::qk_s(i)], s[PT::qk_b(i)], 0, 0, 0);
+    });
+  }
+  if (nsteps > 1) iteration(0, F_{}, T_{}, T_{}, T_{});
+  else iteration(0, F_{}, F_{}, T_{}, T_{});
+  // ---- steady state: every part present
+  for (int j = 1; j + 1 < nsteps; ++j) {
+    if (j & 1) tile_sync(j);
+    iteration(j, T_{}, T_{}, T_{}, F_{});
+  }
+  // ---- the last softmax step (no QK), then PV of the last step
+  if (nsteps > 1) {
+    if ((nsteps - 1) & 1) tile_sync(nsteps - 1);
+    iteration(nsteps - 1, T_{}, F_{}, T_{}, F_{});
+  }
+  if (nsteps & 1) tile_sync(nsteps);
+  iteration(nsteps, T_{}, F_{}, F_{}, F_{});
+  if (resc) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+  }
+
+  // ---- epilogue (as attn_fwd_bf16): O / l -> bf16 (RNE), staged through the wave's
+  // own LDS rows once every wave is done with the K/V stages, stored as whole rows
+  // (non-temporal), rows inside the segment only.
+  const float inv = 1.0f / half_swap_sum(l_run);
+  constexpr int OP = D + 8;
+  static_assert(TL::kWaves * 32 * OP <= TL::kStages * TL::kStageElems, "O staging must fit in the K/V stages");
+  __syncthreads();
+  __bf16* ow = lds + wave * 32 * OP;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      bf16x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(o[ct][4 * r4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(ow + n * OP + ct * 32 + r4 * 8 + 4 * hf) = val;
+    }
+  constexpr int CH = D / 8;
+  constexpr int NU = 32 * CH / 64;
+  static_assert(32 * CH % 64 == 0, "whole store instructions per wave");
+  bf16x8 piece_val[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int cidx = u * 64 + lane;
+    piece_val[u] = *reinterpret_cast<const bf16x8*>(ow + (cidx / CH) * OP + (cidx % CH) * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int cidx = u * 64 + lane;
+    const int row = cidx / CH;
+    if (qmin + row < L)
+      __builtin_nontemporal_store(piece_val[u],
+                                  reinterpret_cast<bf16x8*>(og + static_cast<size_t>(qmin + row) * a.ldo + (cidx % CH) * 8));
+  }
+}
+
+}  // namespace mgattn

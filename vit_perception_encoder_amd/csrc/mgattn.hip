@@ -18,6 +18,7 @@
 
 #include "../../include/mgattn.h"
 #include "attn_bf16.hpp"
+#include "attn_bf16_pipe.hpp"
 #include "attn_decode.hpp"
 #include "attn_f32.hpp"
 #include "plan.hpp"
@@ -279,7 +280,7 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
                        : launch_all(attn_fwd_bf16<64, false>, Bf16Tile<64>::kThreads, plan, args, s);
       case 96:
         return general ? launch_all(attn_fwd_bf16<96, true>, Bf16Tile<96>::kThreads, plan, args, s)
-                       : launch_all(attn_fwd_bf16<96, false>, Bf16Tile<96>::kThreads, plan, args, s);
+                       : launch_all(attn_fwd_bf16_pipe<96>, Bf16Tile<96>::kThreads, plan, args, s);
       case 128:
         return general ? launch_all(attn_fwd_bf16<128, true>, Bf16Tile<128>::kThreads, plan, args, s)
                        : launch_all(attn_fwd_bf16<128, false>, Bf16Tile<128>::kThreads, plan, args, s);

@@ -105,6 +105,34 @@ def _stream(stream) -> int:
     return int(stream.cuda_stream)
 
 
+_ELEM_BYTES = {MGATTN_F32: 4, MGATTN_BF16: 2}
+
+
+def _check_tensor(name: str, t, elem_bytes: int | None, need_bytes: int) -> None:
+    """Refuse, before the C call, a torch tensor the kernels would read or write out
+    of bounds: it must live on a GPU, have the element size of the call's dtype (None:
+    any), and own at least ``need_bytes`` bytes of storage from its data pointer on.
+    Raw integer addresses (and None) are passed through unchecked: the C side only
+    sees pointers."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name}: expected a GPU tensor, got one on {getattr(t, 'device', type(t))}")
+    if elem_bytes is not None and t.element_size() != elem_bytes:
+        raise ValueError(f"{name}: element size {t.element_size()} B does not match the call's dtype "
+                         f"({elem_bytes} B)")
+    have = t.untyped_storage().nbytes() - t.storage_offset() * t.element_size()
+    if need_bytes > have:
+        raise ValueError(f"{name}: the call spans {need_bytes} bytes from the data pointer, the tensor's storage "
+                         f"holds {have}")
+
+
+def _span(rows: int, ld: int, width: int, elem: int) -> int:
+    """Bytes from the first element of row 0 to the end of row rows-1 (rows of
+    `width` elements, `ld` elements apart)."""
+    return 0 if rows <= 0 else ((rows - 1) * ld + width) * elem
+
+
 def _cu_array(cu_seqlens):
     seq = [int(x) for x in cu_seqlens]
     return (ctypes.c_int32 * len(seq))(*seq), len(seq)
@@ -120,6 +148,11 @@ def mgattn_dense(q, k, v, out, cu_seqlens: Sequence[int], n_seg: int, H: int, d:
     cu, ncu = _cu_array(cu_seqlens)
     if ncu < n_seg + 1:
         raise ValueError(f"cu_seqlens has {ncu} entries, n_seg={n_seg} needs {n_seg + 1}")
+    eb = _ELEM_BYTES.get(int(dtype))
+    if eb is not None and n_seg >= 0:
+        T = int(cu[n_seg])
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            _check_tensor(name, t, eb, _span(T, H * d, H * d, eb))
     st = lib.mgattn_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(out), ctypes.cast(cu, ctypes.c_void_p), int(n_seg),
                           int(H), int(d), float(scale), int(causal), int(dtype), _stream(stream))
     if check and st != 0:
@@ -136,12 +169,27 @@ def mgattn_dense_strided(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, c
     cu, ncu = _cu_array(cu_seqlens)
     if ncu < n_seg + 1:
         raise ValueError(f"cu_seqlens has {ncu} entries, n_seg={n_seg} needs {n_seg + 1}")
+    eb = _ELEM_BYTES.get(int(dtype))
+    if eb is not None and n_seg >= 0:
+        T = int(cu[n_seg])
+        for name, t, ld in (("q", q, ldq), ("k", k, ldk), ("v", v, ldv), ("out", out, ldo)):
+            _check_tensor(name, t, eb, _span(T, int(ld), H * d, eb))
     st = lib.mgattn_dense_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
                                   ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), float(scale),
                                   int(causal), int(dtype), _stream(stream))
     if check and st != 0:
         raise MgattnError(st, "mgattn_dense_strided")
     return st
+
+
+def _check_kv(q, k, v, out, ldq, ldk, ldv, ldo, cq, ck, n_seq, Hq, Hkv, d, dtype) -> None:
+    eb = _ELEM_BYTES.get(int(dtype))
+    if eb is None or n_seq < 0:
+        return
+    Tq, Tk = int(cq[n_seq]), int(ck[n_seq])
+    for name, t, rows, ld, width in (("q", q, Tq, ldq, Hq * d), ("k", k, Tk, ldk, Hkv * d),
+                                     ("v", v, Tk, ldv, Hkv * d), ("out", out, Tq, ldo, Hq * d)):
+        _check_tensor(name, t, eb, _span(rows, int(ld), width, eb))
 
 
 def mgattn_attention_kv(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu_seqlens_q: Sequence[int],
@@ -154,6 +202,7 @@ def mgattn_attention_kv(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu
     ck, nk = _cu_array(cu_seqlens_k)
     if nq < n_seq + 1 or nk < n_seq + 1:
         raise ValueError(f"cu_seqlens_q/k need {n_seq + 1} entries")
+    _check_kv(q, k, v, out, ldq, ldk, ldv, ldo, cq, ck, n_seq, Hq, Hkv, d, dtype)
     st = lib.mgattn_attention_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
                                  ctypes.cast(cq, ctypes.c_void_p), ctypes.cast(ck, ctypes.c_void_p), int(n_seq),
                                  int(Hq), int(Hkv), int(d), float(scale), int(window), int(dtype), _stream(stream))
@@ -174,6 +223,8 @@ def mgattn_attention_kv_ws(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int,
     ck, nk = _cu_array(cu_seqlens_k)
     if nq < n_seq + 1 or nk < n_seq + 1:
         raise ValueError(f"cu_seqlens_q/k need {n_seq + 1} entries")
+    _check_kv(q, k, v, out, ldq, ldk, ldv, ldo, cq, ck, n_seq, Hq, Hkv, d, dtype)
+    _check_tensor("workspace", workspace, None, int(workspace_bytes))
     st = lib.mgattn_attention_kv_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
                                     ctypes.cast(cq, ctypes.c_void_p), ctypes.cast(ck, ctypes.c_void_p), int(n_seq),
                                     int(Hq), int(Hkv), int(d), float(scale), int(window), int(dtype), _ptr(workspace),
@@ -264,6 +315,9 @@ def mgattn_window_permute(src, dst, row_bytes: int, grids, win: int, inverse: in
     """Gather rows into window order (inverse=0) or scatter them back (inverse=1)."""
     lib = load_library()
     g, n_img = _grid_array(grids)
+    T = sum(int(gh) * int(gw) for gh, gw in grids)
+    for name, t in (("src", src), ("dst", dst)):
+        _check_tensor(name, t, None, T * int(row_bytes))
     st = lib.mgattn_window_permute(_ptr(src), _ptr(dst), int(row_bytes), ctypes.cast(g, ctypes.c_void_p), n_img,
                                    int(win), int(inverse), _stream(stream))
     if check and st != 0:
@@ -276,6 +330,10 @@ def mgattn_rope2d(x, ldx: int, grids, win: int, H: int, d: int, theta: float, dt
     """In-place 2D rotary embedding of x (token rows of leading dimension ldx)."""
     lib = load_library()
     g, n_img = _grid_array(grids)
+    eb = _ELEM_BYTES.get(int(dtype))
+    if eb is not None:
+        T = sum(int(gh) * int(gw) for gh, gw in grids)
+        _check_tensor("x", x, eb, _span(T, int(ldx), H * d, eb))
     st = lib.mgattn_rope2d(_ptr(x), int(ldx), ctypes.cast(g, ctypes.c_void_p), n_img, int(win), int(H), int(d),
                            float(theta), int(dtype), _stream(stream))
     if check and st != 0:
