@@ -198,9 +198,17 @@ int mgattn_dense_supported(int H, int d, int dtype);
  * arithmetic, no GPU needed; equals the static LDS footprint of the kernel. */
 long mgattn_dense_lds_bytes(int d, int dtype);
 
-/* Queries per workgroup of the (d, dtype) kernel (the q-tile height), or a negative
- * mgattn_status.  Pure host arithmetic. */
+/* Queries per workgroup of the (d, dtype) kernel (the tallest q-tile it uses), or a
+ * negative mgattn_status.  Pure host arithmetic. */
 int mgattn_dense_block_m(int d, int dtype);
+
+/* Queries per workgroup mgattn_dense uses for this segment table (same arguments and
+ * refusals as mgattn_dense_plan), or a negative mgattn_status.  Pure host arithmetic.
+ * The bf16 head_dim-96 kernel takes 256 when the (segment, head, q-tile) units of 256
+ * give at least 256 workgroups (one per CU), else 128, so a short call (one
+ * 1024-token segment of 16 heads: 64 units of 256, 128 of 128) spreads over more CUs;
+ * every other (d, dtype) has the single height of mgattn_dense_block_m. */
+int mgattn_dense_plan_block_m(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal);
 
 /* Introspection of the work split (pure host arithmetic, no GPU needed).
  *

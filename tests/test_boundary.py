@@ -160,6 +160,8 @@ def _expected_tiles(cu, H, bm):
 
 @pytest.mark.parametrize("cu,H,dtype,causal", [
     ([0, 4096], 16, 1, 0),
+    ([0, 1024], 16, 1, 0),
+    ([0, 1024, 2048], 16, 1, 1),
     ([0, 1024, 2048, 3072, 4096], 16, 1, 0),
     ([0, 12288, 16384, 17408], 16, 1, 0),
     ([0, 1, 1, 300, 557, 557, 1000], 3, 1, 1),
@@ -167,7 +169,7 @@ def _expected_tiles(cu, H, bm):
     ([0, 100, 357], 8, 0, 1),
 ])
 def test_plan_is_a_bijection(lib, cu, H, dtype, causal):
-    bm = mg.mgattn_dense_block_m(96, dtype)
+    bm = mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 96, dtype, causal)
     grids = mg.mgattn_dense_plan(cu, len(cu) - 1, H, 96, dtype, causal)
     seen = []
     for li, grid in enumerate(grids):
@@ -179,6 +181,22 @@ def test_plan_is_a_bijection(lib, cu, H, dtype, causal):
                 assert t[1] % 8 == b % 8  # head dealt to XCD b % 8
     assert len(seen) == len(set(seen))
     assert set(seen) == _expected_tiles(cu, H, bm)
+
+
+@pytest.mark.parametrize("cu,H,want", [
+    ([0, 4096], 16, 256),                 # the tower's full layer: 256 workgroups of 256 queries
+    ([0, 1024, 2048, 3072, 4096], 16, 256),  # its window layer
+    ([0, 1024], 16, 128),                 # one 448x448 image: 64 units of 256
+    ([0, 2048], 16, 128),                 # 128 units of 256
+    ([0, 100], 1, 128),                   # nothing fills the chip: the shorter tile
+    ([0, 1024] + [1024 + 64 * i for i in range(1, 49)], 16, 256),  # 49 segments x 16 heads
+])
+def test_plan_block_m_fills_the_chip(lib, cu, H, want):
+    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 96, 1, 0) == want
+    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 64, 1, 0) == 256  # one tile height at d = 64
+    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 96, 0, 0) == 128  # and for f32
+    assert sum(mg.mgattn_dense_plan(cu, len(cu) - 1, H, 96, 1, 0)) == H * sum(
+        -(-(cu[g + 1] - cu[g]) // want) for g in range(len(cu) - 1))
 
 
 def test_plan_orders_longest_first_and_splits(lib):
@@ -200,7 +218,10 @@ def test_plan_orders_longest_first_and_splits(lib):
 def test_plan_causal_puts_last_qtile_first(lib):
     cu = [0, 1000]
     first = mg.mgattn_dense_tile(cu, 1, 1, 96, 1, 1, 0, 0)
-    assert first == (0, 0, 768)
+    bm = mg.mgattn_dense_plan_block_m(cu, 1, 1, 96, 1, 1)
+    assert bm == 128  # one head of 1000 tokens fills nothing: the shorter tile
+    assert first == (0, 0, (999 // bm) * bm)
+    assert mg.mgattn_dense_tile(cu, 1, 64, 96, 1, 1, 0, 0) == (0, 0, 768)  # 64 heads: tiles of 256
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

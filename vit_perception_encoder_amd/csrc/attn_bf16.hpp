@@ -136,21 +136,33 @@ __device__ inline void dma16(const void* g, uint32_t m0) {
 }
 // The same with a wave-uniform base and a per-lane 32-bit byte offset (the scalar-base
 // form): no per-lane 64-bit address arithmetic at issue.
+// The base is passed through readfirstlane: it is wave-uniform by construction, and the
+// "s" constraint is only honoured for values the compiler also proves uniform.
 __device__ inline void dma16s(const void* base, uint32_t off, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(base) : "memory");
+  // (readfirstlane returns a signed int: each half goes back to uint32_t before it is
+  // widened, or bit 31 of the low half would be sign-extended into the high half)
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(off), "s"(bs) : "memory");
 }
 __device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most n (wave-uniform) of this wave's vector-memory operations are
 // outstanding: they complete in issue order, so the older ones are done.  Counts above
-// 16 wait for all.
+// 63 (the counter's range) wait for all.
 #define MGATTN_VMCNT_CASE(k) \
   case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
 __device__ inline void dma_wait_leave(int n) {
   switch (n) {
-    MGATTN_VMCNT_CASE(1) MGATTN_VMCNT_CASE(2) MGATTN_VMCNT_CASE(3) MGATTN_VMCNT_CASE(4)
-    MGATTN_VMCNT_CASE(5) MGATTN_VMCNT_CASE(6) MGATTN_VMCNT_CASE(7) MGATTN_VMCNT_CASE(8)
-    MGATTN_VMCNT_CASE(9) MGATTN_VMCNT_CASE(10) MGATTN_VMCNT_CASE(11) MGATTN_VMCNT_CASE(12)
-    MGATTN_VMCNT_CASE(13) MGATTN_VMCNT_CASE(14) MGATTN_VMCNT_CASE(15) MGATTN_VMCNT_CASE(16)
+    MGATTN_VMCNT_CASE(1) MGATTN_VMCNT_CASE(2) MGATTN_VMCNT_CASE(3) MGATTN_VMCNT_CASE(4) MGATTN_VMCNT_CASE(5) MGATTN_VMCNT_CASE(6) MGATTN_VMCNT_CASE(7) MGATTN_VMCNT_CASE(8)
+    MGATTN_VMCNT_CASE(9) MGATTN_VMCNT_CASE(10) MGATTN_VMCNT_CASE(11) MGATTN_VMCNT_CASE(12) MGATTN_VMCNT_CASE(13) MGATTN_VMCNT_CASE(14) MGATTN_VMCNT_CASE(15) MGATTN_VMCNT_CASE(16)
+    MGATTN_VMCNT_CASE(17) MGATTN_VMCNT_CASE(18) MGATTN_VMCNT_CASE(19) MGATTN_VMCNT_CASE(20) MGATTN_VMCNT_CASE(21) MGATTN_VMCNT_CASE(22) MGATTN_VMCNT_CASE(23) MGATTN_VMCNT_CASE(24)
+    MGATTN_VMCNT_CASE(25) MGATTN_VMCNT_CASE(26) MGATTN_VMCNT_CASE(27) MGATTN_VMCNT_CASE(28) MGATTN_VMCNT_CASE(29) MGATTN_VMCNT_CASE(30) MGATTN_VMCNT_CASE(31) MGATTN_VMCNT_CASE(32)
+    MGATTN_VMCNT_CASE(33) MGATTN_VMCNT_CASE(34) MGATTN_VMCNT_CASE(35) MGATTN_VMCNT_CASE(36) MGATTN_VMCNT_CASE(37) MGATTN_VMCNT_CASE(38) MGATTN_VMCNT_CASE(39) MGATTN_VMCNT_CASE(40)
+    MGATTN_VMCNT_CASE(41) MGATTN_VMCNT_CASE(42) MGATTN_VMCNT_CASE(43) MGATTN_VMCNT_CASE(44) MGATTN_VMCNT_CASE(45) MGATTN_VMCNT_CASE(46) MGATTN_VMCNT_CASE(47) MGATTN_VMCNT_CASE(48)
+    MGATTN_VMCNT_CASE(49) MGATTN_VMCNT_CASE(50) MGATTN_VMCNT_CASE(51) MGATTN_VMCNT_CASE(52) MGATTN_VMCNT_CASE(53) MGATTN_VMCNT_CASE(54) MGATTN_VMCNT_CASE(55) MGATTN_VMCNT_CASE(56)
+    MGATTN_VMCNT_CASE(57) MGATTN_VMCNT_CASE(58) MGATTN_VMCNT_CASE(59) MGATTN_VMCNT_CASE(60) MGATTN_VMCNT_CASE(61) MGATTN_VMCNT_CASE(62) MGATTN_VMCNT_CASE(63)
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
 }

@@ -99,12 +99,14 @@ struct PipeTile {
   static_assert(kNPV >= kDK, "K reads start inside the PV slots");
 };
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+// W waves per workgroup, 32 queries each: 8 for launches that fill the chip, 4 (query
+// tiles of 128) when a launch has too few (segment, head, tile) units.
+template <int D, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16_pipe(KernelArgs a) {
   using TL = Bf16Tile<D>;
   using PT = PipeTile<D>;
-  constexpr int BM = TL::kBlockM, BN = TL::kBlockN;
+  constexpr int BM = 32 * W, BN = TL::kBlockN;
   constexpr int SK = TL::kStepKeys;
   constexpr int NB = PT::kNB, KS = PT::kKS, CT = PT::kCT;
   constexpr int NPV = PT::kNPV, NQK = PT::kNQK, NSLOT = PT::kNSlot;
@@ -112,8 +114,8 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   constexpr int NSTEP = BN / SK;
   constexpr int KP = TL::kKPitch, VP = TL::kVPitch, KSL = TL::kKSlots;
   constexpr int KDMA = TL::kKDma, VDMA = TL::kVDma;
-  constexpr int KDMA_W = (KDMA + TL::kWaves - 1) / TL::kWaves;
-  constexpr int VDMA_W = (VDMA + TL::kWaves - 1) / TL::kWaves;
+  constexpr int KDMA_W = (KDMA + W - 1) / W;
+  constexpr int VDMA_W = (VDMA + W - 1) / W;
   constexpr float kRescaleLog2 = 8.0f;
 
   __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
@@ -148,10 +150,10 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   // consecutive 16-byte slots; wave w issues instructions w, w+8, ...  K slot s is row
   // s/KSL, piece s%KSL (the padding piece D/8 repeats piece D/8-1); V slot s is row
   // s/(D/8), piece s%(D/8).  Rows past the segment end are clamped to its last row.
-  auto k_row = [&](int u) { return ((wave + TL::kWaves * u) * 64 + lane) / KSL; };
-  auto k_off = [&](int u) { return min(((wave + TL::kWaves * u) * 64 + lane) % KSL, D / 8 - 1) * 8; };
-  auto v_row = [&](int u) { return ((wave + TL::kWaves * u) * 64 + lane) / (D / 8); };
-  auto v_off = [&](int u) { return (((wave + TL::kWaves * u) * 64 + lane) % (D / 8)) * 8; };
+  auto k_row = [&](int u) { return ((wave + W * u) * 64 + lane) / KSL; };
+  auto k_off = [&](int u) { return min(((wave + W * u) * 64 + lane) % KSL, D / 8 - 1) * 8; };
+  auto v_row = [&](int u) { return ((wave + W * u) * 64 + lane) / (D / 8); };
+  auto v_off = [&](int u) { return (((wave + W * u) * 64 + lane) % (D / 8)) * 8; };
   uint32_t k_boff[KDMA_W], v_boff[VDMA_W];
 #pragma unroll
   for (int u = 0; u < KDMA_W; ++u)
@@ -169,46 +171,47 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     if (last >= BN - 1) {
 #pragma unroll
       for (int u = 0; u < KDMA_W; ++u) {
-        const int i = wave + TL::kWaves * u;
-        if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA))
+        const int i = wave + W * u;
+        if ((part & 1) && (KDMA % W == 0 || i < KDMA))
           dma16s(kb, k_boff[u], __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
       }
 #pragma unroll
       for (int u = 0; u < VDMA_W; ++u) {
-        const int i = wave + TL::kWaves * u;
-        if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
+        const int i = wave + W * u;
+        if ((part & 2) && (VDMA % W == 0 || i < VDMA))
           dma16s(vb, v_boff[u], __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
       }
       return;
     }
 #pragma unroll
     for (int u = 0; u < KDMA_W; ++u) {
-      const int i = wave + TL::kWaves * u;
-      if ((part & 1) && (KDMA % TL::kWaves == 0 || i < KDMA))
+      const int i = wave + W * u;
+      if ((part & 1) && (KDMA % W == 0 || i < KDMA))
         dma16(kb + static_cast<size_t>(min(k_row(u), last)) * ldk + k_off(u),
               __builtin_amdgcn_readfirstlane(lds_addr(kl + i * 512)));
     }
 #pragma unroll
     for (int u = 0; u < VDMA_W; ++u) {
-      const int i = wave + TL::kWaves * u;
-      if ((part & 2) && (VDMA % TL::kWaves == 0 || i < VDMA))
+      const int i = wave + W * u;
+      if ((part & 2) && (VDMA % W == 0 || i < VDMA))
         dma16(vb + static_cast<size_t>(min(v_row(u), last)) * ldv + v_off(u),
               __builtin_amdgcn_readfirstlane(lds_addr(vl + i * 512)));
     }
   };
-  const int my_kdma = KDMA / TL::kWaves + (wave < KDMA % TL::kWaves ? 1 : 0);
-  const int my_vdma = VDMA / TL::kWaves + (wave < VDMA % TL::kWaves ? 1 : 0);
+  const int my_kdma = KDMA / W + (wave < KDMA % W ? 1 : 0);
+  const int my_vdma = VDMA / W + (wave < VDMA % W ? 1 : 0);
 
   // ---- prologue: Q tile (to the third stage), tiles 0 and 1.  Q rows and K of tile
   // 0 are waited for before the first barrier; V of tile 0 and tile 1 at the barrier
   // of iteration 1.
   constexpr int QDMA = BM * D / 8 / 64;
-  constexpr int QDMA_W = QDMA / TL::kWaves;
-  static_assert(QDMA % TL::kWaves == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  constexpr int QDMA_W = QDMA / W;
+  static_assert(QDMA % W == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  static_assert(W == 4 || W == 8, "4 or 8 waves");
   __bf16* ql = lds + (TL::kStages - 1) * TL::kStageElems;
 #pragma unroll
   for (int u = 0; u < QDMA_W; ++u) {
-    const int i = wave + TL::kWaves * u;
+    const int i = wave + W * u;
     const int slot = i * 64 + lane;
     const int row = min(q0 + slot / (D / 8), L - 1);
     dma16(qg + static_cast<size_t>(row) * a.ldq + (slot % (D / 8)) * 8,
@@ -292,8 +295,10 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     if constexpr (PV) {
       static_for<DV>([&](auto ic) { vf[decltype(ic)::value] = read_v(vt, decltype(ic)::value); });
     }
-    float ma = 0.0f, mb = 0.0f, mc = 0.0f, lsum = 0.0f;
-    float px[16][2];  // probabilities of a score pair, between its exp and its conversion
+    float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // partial row maxima: block b, half h at 2b+h
+    float mc = 0.0f;
+    float lsum[2] = {0.0f, 0.0f};  // two row-sum chains (even and odd score pairs)
+    float px[16][2];               // a score pair between its exponent argument and its conversion
     MGATTN_FENCE();
     static_for<NSLOT>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -316,22 +321,21 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
       if constexpr (QK && k + DK >= NPV && k + DK < NSLOT) kf[k + DK - NPV] = read_k(ks, k + DK - NPV);
       // -- the softmax slice of slot k
       if constexpr (SM) {
-        // slots 0..3: row maximum, two chains of max3 over the 16 scores of each block
+        // slots 0..3: row maximum as four independent max3 chains over 8 scores each
         if constexpr (k < 4) {
-          constexpr int r0 = 4 * k;
-          if constexpr (k == 0) {
-            ma = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-            mb = fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3]));
-          } else {
-            ma = fmaxf(fmaxf(ma, s[0][r0]), fmaxf(s[0][r0 + 1], fmaxf(s[0][r0 + 2], s[0][r0 + 3])));
-            mb = fmaxf(fmaxf(mb, s[1][r0]), fmaxf(s[1][r0 + 1], fmaxf(s[1][r0 + 2], s[1][r0 + 3])));
-          }
+          static_for<4>([&](auto cc) {
+            constexpr int ch = decltype(cc)::value, b = ch / 2, r0 = 8 * (ch % 2);
+            if constexpr (k == 0) mx[ch] = fmaxf(fmaxf(s[b][r0], s[b][r0 + 1]), s[b][r0 + 2]);
+            if constexpr (k == 1) mx[ch] = fmaxf(fmaxf(mx[ch], s[b][r0 + 3]), s[b][r0 + 4]);
+            if constexpr (k == 2) mx[ch] = fmaxf(fmaxf(mx[ch], s[b][r0 + 5]), s[b][r0 + 6]);
+            if constexpr (k == 3) mx[ch] = fmaxf(mx[ch], s[b][r0 + 7]);
+          });
         }
         if constexpr (k == 4) {
           // a step with no visible key for some rows (causal) has maximum -inf; the
           // floor keeps the reference finite (those rows get p = 0 and take alpha = 0
           // at the first step with keys)
-          const float m_blk = fmaxf(half_swap_max(fmaxf(ma, mb)), -1.0e30f);
+          const float m_blk = fmaxf(half_swap_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))), -1.0e30f);
           if constexpr (FIRST) {
             m_run = m_blk;
           } else {
@@ -343,25 +347,31 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
           }
           mc = m_run * c;
         }
-        // probabilities, pair by pair: p = exp2(s*c - m*c), converted to bf16 (RNE)
-        // one slot later and added to the row sum
+        // probabilities, pair by pair, in three stages one slot apart (no stage waits
+        // on the one before it): exponent argument s*c - m*c, p = exp2, then the
+        // conversion to bf16 (RNE) and the row sum
         static_for<16>([&](auto uc) {
           constexpr int u = decltype(uc)::value;
           constexpr int b = u / 8, h2 = (u / 4) % 2, e = 2 * (u % 4);
-          if constexpr (PT::exp_slot(u) + 1 == k) {
+          constexpr int E = PT::exp_slot(u);
+          if constexpr (E + 1 == k) {
             const bf16x2 pr = {static_cast<__bf16>(px[u][0]), static_cast<__bf16>(px[u][1])};
             p[b][h2][e] = pr[0];
             p[b][h2][e + 1] = pr[1];
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+            lsum[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[u & 1], false);
           }
-          if constexpr (PT::exp_slot(u) == k) {
-            px[u][0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e], c, -mc));
-            px[u][1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][8 * h2 + e + 1], c, -mc));
+          if constexpr (E == k) {
+            px[u][0] = __builtin_amdgcn_exp2f(px[u][0]);
+            px[u][1] = __builtin_amdgcn_exp2f(px[u][1]);
+          }
+          if constexpr (E - 1 == k) {
+            px[u][0] = __builtin_fmaf(s[b][8 * h2 + e], c, -mc);
+            px[u][1] = __builtin_fmaf(s[b][8 * h2 + e + 1], c, -mc);
           }
         });
         if constexpr (k == PT::kLSlot) {
-          if constexpr (FIRST) l_run = lsum;
-          else l_run = __builtin_fmaf(l_run, alpha, lsum);
+          if constexpr (FIRST) l_run = lsum[0] + lsum[1];
+          else l_run = __builtin_fmaf(l_run, alpha, lsum[0] + lsum[1]);
         }
       }
       MGATTN_FENCE();
@@ -416,7 +426,7 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   // (non-temporal), rows inside the segment only.
   const float inv = 1.0f / half_swap_sum(l_run);
   constexpr int OP = D + 8;
-  static_assert(TL::kWaves * 32 * OP <= TL::kStages * TL::kStageElems, "O staging must fit in the K/V stages");
+  static_assert(W * 32 * OP <= TL::kStages * TL::kStageElems, "O staging must fit in the K/V stages");
   __syncthreads();
   __bf16* ow = lds + wave * 32 * OP;
 #pragma unroll

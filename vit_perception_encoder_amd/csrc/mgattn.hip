@@ -39,6 +39,20 @@ int block_m_of(int d, int dtype) {
   return dtype == MGATTN_BF16 ? Bf16Tile<96>::kBlockM : F32Tile<96>::kBlockM;
 }
 
+// Query-tile height of one dense call.  The bf16 head_dim-96 kernel runs 8 or 4 waves
+// of 32 queries per workgroup: 256 queries when the (segment, head, tile) units give at
+// least one workgroup per CU, else 128 (a single 1024-token segment of 16 heads is 64
+// units of 256 but 128 of 128, one wave per SIMD on twice the CUs: 25 -> 19 us).
+// Two waves per workgroup (64 queries) ran an order of magnitude slower and are not
+// used.  Other kernels have one tile height.
+constexpr int kFillWorkgroups = 256;  // CUs of an MI355X
+int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype) {
+  if (dtype != MGATTN_BF16 || d != 96) return block_m_of(d, dtype);
+  int64_t units = 0;
+  for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + 255) / 256;
+  return units * H >= kFillWorkgroups ? 256 : 128;
+}
+
 long lds_bytes_of(int d, int dtype) {
   if (dtype == MGATTN_BF16) {
     switch (d) {
@@ -222,8 +236,9 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   const bool general = cuk != nullptr || Hkv != H || window != 0;
   const bool pack = general && dtype == MGATTN_BF16;
   const int H_tiles = pack ? Hkv : H;
+  const int bm = general ? block_m_of(d, dtype) : dense_block_m(cu, n_seg, H, d, dtype);
   std::vector<Launch> plan;
-  if (!make_plan(cu, cuk, n_seg, H_tiles, block_m_of(d, dtype), plan, pack ? H / Hkv : 1)) return MGATTN_ERR_SIZE;
+  if (!make_plan(cu, cuk, n_seg, H_tiles, bm, plan, pack ? H / Hkv : 1)) return MGATTN_ERR_SIZE;
   if (!device_ok()) return MGATTN_ERR_DEVICE;
 
   KernelArgs args;
@@ -279,8 +294,9 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
         return general ? launch_all(attn_fwd_bf16<64, true>, Bf16Tile<64>::kThreads, plan, args, s)
                        : launch_all(attn_fwd_bf16<64, false>, Bf16Tile<64>::kThreads, plan, args, s);
       case 96:
-        return general ? launch_all(attn_fwd_bf16<96, true>, Bf16Tile<96>::kThreads, plan, args, s)
-                       : launch_all(attn_fwd_bf16_pipe<96>, Bf16Tile<96>::kThreads, plan, args, s);
+        if (general) return launch_all(attn_fwd_bf16<96, true>, Bf16Tile<96>::kThreads, plan, args, s);
+        if (bm == 128) return launch_all(attn_fwd_bf16_pipe<96, 4>, 4 * 64, plan, args, s);
+        return launch_all(attn_fwd_bf16_pipe<96, 8>, 8 * 64, plan, args, s);
       case 128:
         return general ? launch_all(attn_fwd_bf16<128, true>, Bf16Tile<128>::kThreads, plan, args, s)
                        : launch_all(attn_fwd_bf16<128, false>, Bf16Tile<128>::kThreads, plan, args, s);
@@ -410,6 +426,12 @@ int mgattn_dense_block_m(int d, int dtype) {
   return block_m_of(d, dtype);
 }
 
+int mgattn_dense_plan_block_m(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal) {
+  const int nl = mgattn_dense_plan(cu_seqlens, n_seg, H, d, dtype, causal, nullptr, 0);
+  if (nl < 0) return nl;
+  return dense_block_m(cu_seqlens, n_seg, H, d, dtype);
+}
+
 int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
                       int64_t* grids, int max_launches) {
   if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
@@ -423,7 +445,8 @@ int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
     if (cu_seqlens[g + 1] < cu_seqlens[g]) return MGATTN_ERR_SEQLENS;
   if (cu_seqlens[n_seg] <= 0) return MGATTN_ERR_SEQLENS;
   std::vector<Launch> plan;
-  if (!make_plan(cu_seqlens, nullptr, n_seg, H, block_m_of(d, dtype), plan)) return MGATTN_ERR_SIZE;
+  if (!make_plan(cu_seqlens, nullptr, n_seg, H, dense_block_m(cu_seqlens, n_seg, H, d, dtype), plan))
+    return MGATTN_ERR_SIZE;
   for (int i = 0; i < static_cast<int>(plan.size()) && i < max_launches; ++i)
     if (grids) grids[i] = plan[i].grid;
   return static_cast<int>(plan.size());
@@ -435,9 +458,10 @@ int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
   const int nl = mgattn_dense_plan(cu_seqlens, n_seg, H, d, dtype, causal, nullptr, 0);
   if (nl < 0) return nl;
   std::vector<Launch> plan;
-  make_plan(cu_seqlens, nullptr, n_seg, H, block_m_of(d, dtype), plan);
+  const int bm = dense_block_m(cu_seqlens, n_seg, H, d, dtype);
+  make_plan(cu_seqlens, nullptr, n_seg, H, bm, plan);
   if (launch < 0 || launch >= nl || block < 0 || block >= plan[launch].grid) return MGATTN_ERR_SIZE;
-  const Tile t = decode_tile(plan[launch].table, H, block_m_of(d, dtype), causal, static_cast<int>(block));
+  const Tile t = decode_tile(plan[launch].table, H, bm, causal, static_cast<int>(block));
   if (!t.valid) return 0;
   seg_head_q0[0] = plan[launch].orig[t.slot];
   seg_head_q0[1] = t.head;

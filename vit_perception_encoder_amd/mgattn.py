@@ -28,7 +28,7 @@ STATUS_NAMES = {
 
 EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_attention_kv", "mgattn_attention_kv_ws",
            "mgattn_attention_kv_workspace", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
-           "mgattn_dense_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
+           "mgattn_dense_block_m", "mgattn_dense_plan_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
            "mgattn_window_permute", "mgattn_rope2d", "mgattn_version"]
 
 
@@ -72,6 +72,8 @@ def load_library(path: str | os.PathLike | None = None):
     lib.mgattn_dense_lds_bytes.argtypes = [i32, i32]
     lib.mgattn_dense_block_m.restype = i32
     lib.mgattn_dense_block_m.argtypes = [i32, i32]
+    lib.mgattn_dense_plan_block_m.restype = i32
+    lib.mgattn_dense_plan_block_m.argtypes = [vp, i32, i32, i32, i32, i32]
     lib.mgattn_dense_plan.restype = i32
     lib.mgattn_dense_plan.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32]
     lib.mgattn_dense_tile.restype = i32
@@ -261,6 +263,17 @@ def mgattn_dense_lds_bytes(d: int, dtype: int) -> int:
 
 def mgattn_dense_block_m(d: int, dtype: int) -> int:
     return load_library().mgattn_dense_block_m(int(d), int(dtype))
+
+
+def mgattn_dense_plan_block_m(cu_seqlens, n_seg: int, H: int, d: int, dtype: int, causal: int = 0) -> int:
+    """Queries per workgroup mgattn_dense uses for this segment table (raises on refusal)."""
+    lib = load_library()
+    cu, _ = _cu_array(cu_seqlens)
+    r = lib.mgattn_dense_plan_block_m(ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), int(dtype),
+                                      int(causal))
+    if r < 0:
+        raise MgattnError(r, "mgattn_dense_plan_block_m")
+    return int(r)
 
 
 def mgattn_dense_plan(cu_seqlens, n_seg: int, H: int, d: int, dtype: int, causal: int = 0) -> list[int]:
