@@ -74,15 +74,28 @@ def traffic_per_launch():
 
 
 def host_threads() -> int:
+    """Every core this process may run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return max(1, os.cpu_count() or 1)
 
 
-def cpu_baseline(layer_cases):
-    """The f64 oracle, as it stands, on whole full-attention layers of the schedule."""
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu prints it), from /proc/cpuinfo."""
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layer_cases, one_thread_case):
+    """The f64 oracle, as it stands, on whole full-attention layers of the schedule,
+    on every host core; plus one 1024-token layer on a single thread (a per-core
+    figure)."""
     from oracle import oracle as orc
 
     threads = host_threads()
@@ -92,12 +105,20 @@ def cpu_baseline(layer_cases):
         outs.append(orc.attention(q, k, v, c.cu_seqlens, c.H, c.d, c.scale, n_threads=threads))
         flops += c.flops()
     dt = time.perf_counter() - t0
-    names = ", ".join(c.name for c in layer_cases)
+    c = one_thread_case
+    q, k, v = (x.reshape(c.T, c.H, c.d) for x in (c.q, c.k, c.v))
+    t1 = time.perf_counter()
+    orc.attention(q, k, v, c.cu_seqlens, c.H, c.d, c.scale, n_threads=1)
+    dt1 = time.perf_counter() - t1
+    names = ", ".join(c_.name for c_ in layer_cases)
     return outs, {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                  "seconds": dt,
+                  "seconds": dt, "host_cores": os.cpu_count(), "cpu_model": cpu_model(),
                   "sample": f"{len(layer_cases)} full-attention layers of the schedule ({names}; each 1 segment x "
                             f"4096 tokens, H=16, d=96, bf16 inputs widened to f64), whole outputs, "
-                            f"{flops / 1e9:.1f} GFLOP"}
+                            f"{flops / 1e9:.1f} GFLOP, {threads} threads",
+                  "one_thread": {"value": c.flops() / dt1 / 1e12, "unit": "TFLOP/s", "seconds": dt1,
+                                 "sample": f"{c.name}: one 1024-token segment, H=16, d=96, bf16 inputs, whole "
+                                           f"output, {c.flops() / 1e9:.2f} GFLOP, 1 thread"}}
 
 
 def time_launches(torch, fn, reps: int = 30, warm: int = 10) -> float:
@@ -456,7 +477,7 @@ def main() -> int:
     parity = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the f64 CPU oracle on {len(host_cpu)} full layers", file=sys.stderr, flush=True)
-        wants, cpu = cpu_baseline(host_cpu)
+        wants, cpu = cpu_baseline(host_cpu, wl.config_full448())
         parity = 0.0
         for l, want in zip(cpu_layers, wants):
             q, k, v, cu, nseg, _, _ = layers[l]

@@ -44,7 +44,8 @@ def load(path: str | os.PathLike | None = None):
     global _lib
     if path is None and _lib is not None:
         return _lib
-    lib = ctypes.CDLL(str(path if path is not None else build()))
+    override = os.environ.get("MGATTN_ORACLE_LIB")  # e.g. a sanitizer build, for the host checks
+    lib = ctypes.CDLL(str(path if path is not None else (override or build())))
     vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     lib.mgattn_oracle_f64.restype = i32
     lib.mgattn_oracle_f64.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, i32, i32, i32]

@@ -4,9 +4,10 @@ accumulation) and <= 1e-4 for f32 inputs.
 
 Small cases are compared element by element over the whole output.  Full-size cases
 (the 50-layer tower at 4096 tokens, the ragged 16k/17k-token batches) run in the
-same launch configuration as the benchmark and are compared on sampled rows the
-oracle computes one by one: every segment's first and last rows, rows on both sides
-of each q-tile edge, and random rows."""
+same launch configuration as the benchmark: every layer on sampled rows the oracle
+computes one by one (every segment's first and last rows, rows on both sides of each
+q-tile edge, and random rows), and the largest layers (tower layers 3 and 0, both
+ragged batches' full and window layers) on the whole output."""
 from __future__ import annotations
 
 import numpy as np
@@ -90,6 +91,24 @@ def test_config5_ragged(torch, which):
     qkv = wl.ragged_inputs(which)
     for kind in ("full", "window"):
         _sampled_check(torch, wl.ragged_case(which, kind, qkv), n_random=256, seed=7)
+
+
+# ------------------------------------------------- whole outputs at the full sizes
+# The sampled checks above run every layer; these compare every element of the
+# largest layers against the oracle (about a minute of oracle time on 16 host cores).
+
+@pytest.mark.parametrize("layer", [3, 0])
+def test_config4_tower_layers_whole_output(torch, layer):
+    """Tower layer 3 (one 4096-token segment) and layer 0 (four 1024-token windows),
+    every element, in the benchmark's launch configuration."""
+    _full_check(torch, wl.tower_layer(layer), guard_rows=2)
+
+
+@pytest.mark.parametrize("which,kind", [("5a", "full"), ("5a", "window"), ("5b", "full"), ("5b", "window")])
+def test_config5_ragged_whole_output(torch, which, kind):
+    """The ragged multi-image batches (segments of 12,288 / 10,752 tokens and clipped
+    windows, 5% of Q and K rows scaled x8), every element."""
+    _full_check(torch, wl.ragged_case(which, kind, wl.ragged_inputs(which)), guard_rows=2)
 
 
 # ------------------------------------------------------------------------ edge cases

@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "plan.hpp"
+#include "schedule.hpp"
 
 namespace mgattn {
 
@@ -75,31 +76,17 @@ struct KernelArgs {
 };
 
 template <int D>
-struct Bf16Tile {
+struct Bf16Tile : sched::Geometry<D> {
+  using G = sched::Geometry<D>;
   static constexpr int kWaves = 8;
   static constexpr int kQBlocks = 1;                     // 32-query blocks per wave
   static constexpr int kBlockM = kWaves * kQBlocks * 32; // queries per workgroup
-  static constexpr int kBlockN = 128;                    // keys per LDS tile
-  static constexpr int kStepKeys = 64;                   // keys per softmax step
   static constexpr int kThreads = kWaves * 64;
-  static constexpr int kKSlots = D / 8 + 1;              // 16-byte slots per K row (+1 pad)
-  static constexpr int kKPitch = kKSlots * 8;            // K row pitch (elements)
-  static constexpr int kVPitch = D;                      // V row pitch (elements)
-  static constexpr int kKElems = kBlockN * kKPitch;
-  static constexpr int kVElems = kBlockN * kVPitch;
-  static constexpr int kStageElems = kKElems + kVElems;
-  // LDS stages: three when they fit in the 160 KB of a CU (head_dim <= 96), so a tile
-  // is published a full step before its first read; two otherwise.
-  static constexpr int kStages = (3 * kStageElems * 2 <= 160 * 1024) ? 3 : 2;
-  static constexpr int kLdsBytes = kStages * kStageElems * 2;
-  // LDS DMA instructions (64 lanes x 16 bytes) per tile
-  static constexpr int kKDma = (kBlockN * kKSlots + 63) / 64;
-  static constexpr int kVDma = kBlockN * D / 8 / 64;
   static_assert(D % 32 == 0 && D >= 32 && D <= 128, "head_dim must be a multiple of 32 up to 128");
-  static_assert(kBlockN % kStepKeys == 0 && kStepKeys % 32 == 0, "LDS tile must hold whole softmax steps");
-  static_assert((kBlockN * D / 8) % 64 == 0, "V tile must be whole DMA instructions");
-  static_assert(kKElems % 8 == 0 && kStageElems % 8 == 0, "LDS regions must stay 16-byte aligned");
-  static_assert(kBlockN * kKSlots % 64 == 0, "K tile must be whole DMA instructions");
+  static_assert(G::kBlockN % G::kStepKeys == 0 && G::kStepKeys % 32 == 0, "LDS tile must hold whole softmax steps");
+  static_assert((G::kBlockN * D / 8) % 64 == 0, "V tile must be whole DMA instructions");
+  static_assert(G::kKElems % 8 == 0 && G::kStageElems % 8 == 0, "LDS regions must stay 16-byte aligned");
+  static_assert(G::kBlockN * G::kKSlots % 64 == 0, "K tile must be whole DMA instructions");
 };
 
 // Exchange with lane l^32 and combine (max or sum) -- one v_permlane32_swap.
@@ -463,7 +450,7 @@ void attn_fwd_bf16(KernelArgs a) {
   // I(t) = max(2tN-4, 2N(t-S+1)+2): two phases of latency when the buffer it replaces
   // (tile t-S, last read in phase 2N(t-S+1)+1) is already free.
   constexpr int N2 = 2 * NSTEP;
-  auto issue_phase = [&](int t) { return max(N2 * t - 4, N2 * (t - TL::kStages + 1) + 2); };
+  auto issue_phase = [&](int t) { return sched::phased_issue_phase(t, NSTEP, TL::kStages); };
   int t_issue = 0, t_wait = 0;
   // The workgroup's Q tile goes to the last stage by LDS DMA as well (whole rows,
   // 16 bytes per lane; rows past the segment end clamped), together with the first
@@ -533,7 +520,7 @@ void attn_fwd_bf16(KernelArgs a) {
   };
   auto stage_end = [&](int p) {
     if (p == 0) dma_wait_leave(TL::kStages >= 3 && t_issue >= 2 ? my_kdma : 0);  // Q rows 128.., V of tile 0
-    if (t_wait < ntiles && N2 * t_wait - 2 == p) {
+    if (t_wait < ntiles && sched::phased_wait_phase(t_wait, NSTEP) == p) {
       dma_wait();
       ++t_wait;
     }

@@ -44,6 +44,7 @@
 
 #include "attn_bf16.hpp"
 #include "plan.hpp"
+#include "schedule.hpp"
 
 namespace mgattn {
 
@@ -219,6 +220,7 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   }
   issue_tile(0, 1);
   issue_tile(0, 2);
+  static_assert(sched::kPipePrologueTiles == 2, "tiles 0 and 1 before the first barrier");
   if (ntiles > 1) issue_tile(1, 3);
   dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + my_vdma : 0));
   __syncthreads();
@@ -288,8 +290,9 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
       }
     }
     if constexpr (SM) mask(j);
-    const __bf16* vt = PV ? stage_of(j - 1) + TL::kKElems + ((j - 1) % NSTEP) * NB * 32 * VP : lds;
-    const __bf16* ks = QK ? stage_of(j + 1) + ((j + 1) % NSTEP) * NB * 32 * KP : lds;
+    const int jv = sched::pipe_v_step(j), jk = sched::pipe_k_step(j);
+    const __bf16* vt = PV ? stage_of(jv) + TL::kKElems + (jv % NSTEP) * NB * 32 * VP : lds;
+    const __bf16* ks = QK ? stage_of(jk) + (jk % NSTEP) * NB * 32 * KP : lds;
     bf16x8 vf[NPV];
     bf16x8 kf[NQK];
     if constexpr (PV) {
@@ -380,12 +383,13 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   };
 
   auto tile_sync = [&](int j) {  // start of odd iteration j = 2t+1
-    const int t = j >> 1;
+    if (!sched::pipe_syncs(j)) return;
     dma_wait();  // this wave's DMA of tile t+1
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + 2 < ntiles) issue_tile(t + 2, 3);
+    const int tn = sched::pipe_issue_tile(j);
+    if (tn < ntiles) issue_tile(tn, 3);
   };
 
   using T_ = std::true_type;
@@ -406,15 +410,15 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   else iteration(0, F_{}, F_{}, T_{}, T_{});
   // ---- steady state: every part present
   for (int j = 1; j + 1 < nsteps; ++j) {
-    if (j & 1) tile_sync(j);
+    tile_sync(j);
     iteration(j, T_{}, T_{}, T_{}, F_{});
   }
   // ---- the last softmax step (no QK), then PV of the last step
   if (nsteps > 1) {
-    if ((nsteps - 1) & 1) tile_sync(nsteps - 1);
+    tile_sync(nsteps - 1);
     iteration(nsteps - 1, T_{}, F_{}, T_{}, F_{});
   }
-  if (nsteps & 1) tile_sync(nsteps);
+  tile_sync(nsteps);
   iteration(nsteps, T_{}, F_{}, F_{}, F_{});
   if (resc) {
 #pragma unroll

@@ -1,0 +1,74 @@
+// LDS staging schedules of the bf16 attention kernels: which K/V tile goes into which
+// LDS stage, when its DMA is issued and waited for, and which step's keys and values a
+// wave reads in each part of its program.  Plain constexpr functions with no GPU
+// dependency, shared by the kernels and by a host model that replays every wave's
+// program and checks that no stage is read before its DMA is waited for and published
+// by a barrier, and none is overwritten before its last read.
+#pragma once
+
+#ifdef __HIPCC__
+#define MGATTN_HD __host__ __device__
+#else
+#define MGATTN_HD
+#endif
+
+namespace mgattn {
+namespace sched {
+
+constexpr MGATTN_HD int imax(int a, int b) { return a > b ? a : b; }
+
+// Geometry shared by both kernels (bf16, 128-key tiles, 64-key softmax steps).
+template <int D>
+struct Geometry {
+  static constexpr int kBlockN = 128;                    // keys per LDS tile
+  static constexpr int kStepKeys = 64;                   // keys per softmax step
+  static constexpr int kStepsPerTile = kBlockN / kStepKeys;
+  static constexpr int kKSlots = D / 8 + 1;              // 16-byte slots per K row (+1 pad)
+  static constexpr int kKPitch = kKSlots * 8;            // K row pitch (elements)
+  static constexpr int kVPitch = D;                      // V row pitch (elements)
+  static constexpr int kKElems = kBlockN * kKPitch;
+  static constexpr int kVElems = kBlockN * kVPitch;
+  static constexpr int kStageElems = kKElems + kVElems;
+  // three stages when they fit in the 160 KB of a CU (head_dim <= 96), else two
+  static constexpr int kStages = (3 * kStageElems * 2 <= 160 * 1024) ? 3 : 2;
+  static constexpr int kLdsBytes = kStages * kStageElems * 2;
+  // LDS DMA instructions (64 lanes x 16 bytes) per tile
+  static constexpr int kKDma = (kBlockN * kKSlots + 63) / 64;
+  static constexpr int kVDma = kBlockN * D / 8 / 64;
+  // of which wave w of W issues instructions w, w + W, ...
+  static constexpr MGATTN_HD int k_dma_of(int w, int W) { return kKDma / W + (w < kKDma % W ? 1 : 0); }
+  static constexpr MGATTN_HD int v_dma_of(int w, int W) { return kVDma / W + (w < kVDma % W ? 1 : 0); }
+  // Q tile of bm rows, 16 bytes per lane
+  static constexpr MGATTN_HD int q_dma(int bm) { return bm * D / 8 / 64; }
+};
+
+// ---- the phased kernel (attn_fwd_bf16): two wave groups one phase apart, a barrier
+// closing every phase.  A wave's slots are MFMA(0), VALU(0), MFMA(1), ..., VALU(n-1),
+// MFMA(n); the leading group (waves 0..W/2-1) runs slot i in phase i, the trailing one
+// in phase i+1.  MFMA(0) reads the Q fragments and K of step 0; VALU(j) reads (part of)
+// K of step j+1; MFMA(j) reads the rest of K of step j (head_dim 128) and V of step j-1.
+// Tile t (steps 2t, 2t+1 at 64 keys per step) sits in stage t % stages; its DMA is
+// issued at the start of phase phased_issue_phase(t) (its V one phase later with three
+// stages) and waited for at the end of phase phased_wait_phase(t); the Q tile sits in
+// the last stage.  Tile 0 and the Q tile are issued before phase 0: the leading
+// group's Q rows and K of tile 0 are waited for before the first barrier, the rest at
+// the end of phase 0.
+constexpr MGATTN_HD int phased_issue_phase(int t, int steps_per_tile, int stages) {
+  return imax(2 * steps_per_tile * t - 4, 2 * steps_per_tile * (t - stages + 1) + 2);
+}
+constexpr MGATTN_HD int phased_wait_phase(int t, int steps_per_tile) { return 2 * steps_per_tile * t - 2; }
+
+// ---- the pipelined kernel (attn_fwd_bf16_pipe): iteration j runs PV of step j-1, QK
+// of step j+1 and the softmax of step j; QK of step 0 runs before iteration 0.  Tile t
+// sits in stage t % 3 (the Q tile in stage 2 until tile 2 arrives).  Tiles 0 and 1
+// are issued before the first barrier, which publishes Q and K of tile 0; odd
+// iterations open with a wait for all of the wave's DMA, a barrier, and the issue of
+// tile pipe_issue_tile(j).
+constexpr MGATTN_HD int pipe_k_step(int j) { return j + 1; }       // K read by iteration j (QK)
+constexpr MGATTN_HD int pipe_v_step(int j) { return j - 1; }       // V read by iteration j (PV)
+constexpr MGATTN_HD bool pipe_syncs(int j) { return (j & 1) != 0; }
+constexpr MGATTN_HD int pipe_issue_tile(int j) { return (j >> 1) + 2; }
+constexpr int kPipePrologueTiles = 2;
+
+}  // namespace sched
+}  // namespace mgattn

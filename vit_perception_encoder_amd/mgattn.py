@@ -46,7 +46,8 @@ def load_library(path: str | os.PathLike | None = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = Path(path) if path is not None else LIB_PATH
+    # MGATTN_LIB names another build of the same library (e.g. host code under sanitizers)
+    p = Path(path) if path is not None else Path(os.environ.get("MGATTN_LIB", LIB_PATH))
     if not p.exists():
         raise ImportError(f"mgattn HIP library not built: {p} is missing "
                           "(run `python -m vit_perception_encoder_amd.build`)")
