@@ -59,7 +59,8 @@ typedef enum {
                                 a multiple of 16 bytes (also: a bad row_bytes) */
   MGATTN_ERR_GRID = -14,     /* a patch grid is empty, more than 64 images, a window
                                 below its minimum, or a flag is not 0 or 1 */
-  MGATTN_ERR_WINDOW = -15    /* mgattn_attention_kv: window < 0 */
+  MGATTN_ERR_WINDOW = -15,   /* mgattn_attention_kv: window < 0 */
+  MGATTN_ERR_SCRATCH = -16   /* mgattn_attention_kv_noalloc: more scratch than it holds */
 } mgattn_status;
 
 /*
@@ -185,6 +186,28 @@ int mgattn_attention_kv_ws(const void* q, const void* k, const void* v, void* ou
  * host array and shape checks of mgattn_attention_kv). */
 long mgattn_attention_kv_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq,
                                    int Hq, int Hkv, int d, int window, int dtype);
+
+/* mgattn_attention_kv_noalloc: mgattn_attention_kv_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and result as mgattn_attention_kv without the
+ * workspace: the partial results of the decode key splits go to a scratch array the
+ * library holds in each GPU's memory (a static device array of
+ * mgattn_attention_kv_noalloc_scratch_bytes() = 4,259,840 bytes, the most any call
+ * needs under the split rule, resolved once per device), so
+ * the call allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * A call that needs more than that is refused with MGATTN_ERR_SCRATCH before anything
+ * is launched (mgattn_attention_kv_workspace gives the need).  Every call on one GPU
+ * shares that GPU's scratch and leaves its contents behind (nothing in it needs to
+ * start at zero): calls that overlap on one GPU (different streams without ordering)
+ * race; calls in stream order do not. */
+int mgattn_attention_kv_noalloc(const void* q, const void* k, const void* v, void* out,
+                                int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int n_seq, int Hq, int Hkv, int d, float scale, int window,
+                                int dtype, void* stream);
+
+/* Bytes of the per-device scratch of mgattn_attention_kv_noalloc (its size limit). */
+long mgattn_attention_kv_noalloc_scratch_bytes(void);
 
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char* mgattn_strerror(int status);

@@ -14,6 +14,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "../../include/mgattn.h"
@@ -311,6 +312,35 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   return MGATTN_ERR_HEAD_DIM;
 }
 
+// ---- scratch of mgattn_attention_kv_noalloc: the partial results of the decode key
+// splits live in a file-scope device array instead of a caller's workspace.  Each
+// GPU the library runs on holds its own copy until the process ends; host code only
+// ever passes the device address found by hipGetSymbolAddress on that device.
+// Size: the split rule keeps (sequence, key/value head, split) triples within
+// kDecodeTargetWgs per launch, each writing 32 query columns of d + 2 floats, so no
+// call needs more than 256 x 32 x 130 x 4 bytes = 4.06 MiB at head_dim 128; the entry
+// point still refuses a larger need by name.
+constexpr size_t kScratchBytes = size_t(kDecodeTargetWgs) * 32 * (128 + 2) * sizeof(float);
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (resolved once per device), or NULL.
+void* scratch_device_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -329,6 +359,27 @@ int mgattn_attention_kv(const void* q, const void* k, const void* v, void* out, 
   return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1, window,
                 dtype, stream);
 }
+
+int mgattn_attention_kv_noalloc(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk,
+                                int64_t ldv, int64_t ldo, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int n_seq, int Hq, int Hkv, int d, float scale, int window, int dtype, void* stream) {
+  const long need = mgattn_attention_kv_workspace(cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, window, dtype);
+  if (need < 0) return static_cast<int>(need);
+  if (static_cast<size_t>(need) > kScratchBytes) return MGATTN_ERR_SCRATCH;
+  if (need == 0)
+    return mgattn_attention_kv(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale,
+                               window, dtype, stream);
+  const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1,
+                          window, dtype);
+  if (st != MGATTN_OK) return st;
+  if (!device_ok()) return MGATTN_ERR_DEVICE;
+  void* ws = scratch_device_ptr();
+  if (!ws) return MGATTN_ERR_DEVICE;
+  return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens_q, cu_seqlens_k, n_seq, Hq, Hkv, d, scale, 1, window,
+                dtype, stream, ws, static_cast<size_t>(need));
+}
+
+long mgattn_attention_kv_noalloc_scratch_bytes(void) { return static_cast<long>(kScratchBytes); }
 
 long mgattn_attention_kv_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int n_seq, int Hq,
                                    int Hkv, int d, int window, int dtype) {
@@ -403,6 +454,8 @@ const char* mgattn_strerror(int status) {
     case MGATTN_ERR_DEVICE: return "the current device is not a gfx950 (MI355X) GPU";
     case MGATTN_ERR_SIZE: return "a segment spans more than 2^31 bytes, or the grid is too large";
     case MGATTN_ERR_WINDOW: return "window must be >= 0";
+    case MGATTN_ERR_SCRATCH: return "the call needs more scratch than mgattn_attention_kv_noalloc holds "
+                                    "(mgattn_attention_kv_noalloc_scratch_bytes); use mgattn_attention_kv_ws";
     case MGATTN_ERR_GRID:
       return "a patch grid is empty, more than 64 images, a window below 1, or inverse not 0 or 1";
     case MGATTN_ERR_STRIDE:

@@ -23,10 +23,11 @@ STATUS_NAMES = {
     -4: "MGATTN_ERR_HEADS", -5: "MGATTN_ERR_SEQLENS", -6: "MGATTN_ERR_SEGMENTS",
     -7: "MGATTN_ERR_ALIAS", -8: "MGATTN_ERR_ALIGN", -9: "MGATTN_ERR_SCALE",
     -10: "MGATTN_ERR_LAUNCH", -11: "MGATTN_ERR_DEVICE", -12: "MGATTN_ERR_SIZE", -13: "MGATTN_ERR_STRIDE",
-    -14: "MGATTN_ERR_GRID", -15: "MGATTN_ERR_WINDOW",
+    -14: "MGATTN_ERR_GRID", -15: "MGATTN_ERR_WINDOW", -16: "MGATTN_ERR_SCRATCH",
 }
 
 EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_attention_kv", "mgattn_attention_kv_ws",
+           "mgattn_attention_kv_noalloc", "mgattn_attention_kv_noalloc_scratch_bytes",
            "mgattn_attention_kv_workspace", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
            "mgattn_dense_block_m", "mgattn_dense_plan_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
            "mgattn_window_permute", "mgattn_rope2d", "mgattn_version"]
@@ -63,6 +64,11 @@ def load_library(path: str | os.PathLike | None = None):
     lib.mgattn_attention_kv_ws.restype = i32
     lib.mgattn_attention_kv_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i32, i32, i32, i32, f32, i32,
                                            i32, vp, ctypes.c_size_t, vp]
+    lib.mgattn_attention_kv_noalloc.restype = i32
+    lib.mgattn_attention_kv_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, i32, i32, i32, i32, f32,
+                                                i32, i32, vp]
+    lib.mgattn_attention_kv_noalloc_scratch_bytes.restype = ctypes.c_long
+    lib.mgattn_attention_kv_noalloc_scratch_bytes.argtypes = []
     lib.mgattn_attention_kv_workspace.restype = ctypes.c_long
     lib.mgattn_attention_kv_workspace.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32]
     lib.mgattn_strerror.restype = ctypes.c_char_p
@@ -235,6 +241,31 @@ def mgattn_attention_kv_ws(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int,
     if check and st != 0:
         raise MgattnError(st, "mgattn_attention_kv_ws")
     return st
+
+
+def mgattn_attention_kv_noalloc(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu_seqlens_q: Sequence[int],
+                                cu_seqlens_k: Sequence[int], n_seq: int, Hq: int, Hkv: int, d: int, scale: float,
+                                window: int, dtype: int, stream=None, check: bool = True) -> int:
+    """mgattn_attention_kv_ws without a workspace argument: the key-split partial
+    results go to the library's per-device scratch (see mgattn_attention_kv_noalloc
+    in include/mgattn.h); nothing is allocated."""
+    lib = load_library()
+    cq, nq = _cu_array(cu_seqlens_q)
+    ck, nk = _cu_array(cu_seqlens_k)
+    if nq < n_seq + 1 or nk < n_seq + 1:
+        raise ValueError(f"cu_seqlens_q/k need {n_seq + 1} entries")
+    _check_kv(q, k, v, out, ldq, ldk, ldv, ldo, cq, ck, n_seq, Hq, Hkv, d, dtype)
+    st = lib.mgattn_attention_kv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv),
+                                         int(ldo), ctypes.cast(cq, ctypes.c_void_p), ctypes.cast(ck, ctypes.c_void_p),
+                                         int(n_seq), int(Hq), int(Hkv), int(d), float(scale), int(window), int(dtype),
+                                         _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_attention_kv_noalloc")
+    return st
+
+
+def mgattn_attention_kv_noalloc_scratch_bytes() -> int:
+    return int(load_library().mgattn_attention_kv_noalloc_scratch_bytes())
 
 
 def mgattn_attention_kv_workspace(cu_seqlens_q: Sequence[int], cu_seqlens_k: Sequence[int], n_seq: int, Hq: int,
