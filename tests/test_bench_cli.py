@@ -36,6 +36,9 @@ def test_a_multi_rank_launch_is_refused_too():
 
 
 def test_traffic_summary_is_used_only_for_its_kernel_sources():
+    if not bench.TRAFFIC_FILE.exists():  # no counters taken on this kernel yet: the bench reports null
+        assert bench.traffic_per_launch() is None
+        return
     t = json.loads(bench.TRAFFIC_FILE.read_text())
     if t["kernel_source_sha256"] == bench.kernel_source_hash():
         assert bench.traffic_per_launch() == t["hbm_bytes_per_launch"]

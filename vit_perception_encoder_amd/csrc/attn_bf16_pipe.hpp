@@ -103,7 +103,7 @@ struct PipeTile {
 // W waves per workgroup, 32 queries each: 8 for launches that fill the chip, 4 (query
 // tiles of 128) when a launch has too few (segment, head, tile) units.
 template <int D, int W>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W == 8 ? 2 : 1, 2)))
 void attn_fwd_bf16_pipe(KernelArgs a) {
   using TL = Bf16Tile<D>;
   using PT = PipeTile<D>;
