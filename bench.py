@@ -205,6 +205,30 @@ def token_path(torch, mg, wl, layers):
         ms = best[name]
         res[f"{name}_qkv_full_layer_4096"] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
                                              "frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    # the tower's RoPE + attention per layer (tokens in 32x32-window order of the 64x64
+    # grid, q|k|v merged): the RoPE pass over q and k then the attention, against
+    # mgattn_dense_rope2d (k rotated in place, q rotated as the attention loads it)
+    grid64 = [(64, 64)]
+    for lname, li in (("full_layer_4096", 3), ("window_layer_4x1024", 0)):
+        cu_l, nseg_l, fl_l = layers[li][3], layers[li][4], layers[li][5]
+
+        def unfused():
+            mg.mgattn_rope2d(qkv[:, :2 * row], qkv.stride(0), grid64, 32, 2 * H, d, THETA, mg.MGATTN_BF16, stream)
+            mg.mgattn_dense_strided(qkv[:, :row], qkv[:, row:2 * row], qkv[:, 2 * row:], out, qkv.stride(0),
+                                    qkv.stride(0), qkv.stride(0), row, cu_l, nseg_l, H, d, wl.SCALE, 0, mg.MGATTN_BF16,
+                                    stream)
+
+        def fused():
+            mg.mgattn_dense_rope2d(qkv[:, :row], qkv[:, row:2 * row], qkv[:, 2 * row:], out, qkv.stride(0),
+                                   qkv.stride(0), qkv.stride(0), row, cu_l, nseg_l, H, d, wl.SCALE, 0, mg.MGATTN_BF16,
+                                   grid64, 32, THETA, stream)
+
+        bt = {"unfused": float("inf"), "fused": float("inf")}
+        for _ in range(3):
+            for name, fn in (("unfused", unfused), ("fused", fused)):
+                bt[name] = min(bt[name], time_launches(torch, fn))
+        res[f"rope_attention_{lname}"] = {"unfused_ms": bt["unfused"], "fused_ms": bt["fused"],
+                                          "fused_tflops": fl_l / (bt["fused"] * 1e-3) / 1e12}
     for name, grids in (("tower_64x64", [(64, 64)]), ("ragged_17408", [(128, 96), (64, 64), (32, 32)])):
         T = sum(gh * gw for gh, gw in grids)
         x = torch.randn(T, row, device=dev).to(torch.bfloat16)

@@ -301,6 +301,23 @@ int mgattn_window_permute(const void* src, void* dst, int64_t row_bytes, const i
 int mgattn_rope2d(void* x, int64_t ldx, const int32_t* grids, int n_img, int win, int H, int d, float theta,
                   int dtype, void* stream);
 
+/* mgattn_dense_strided over 2D-RoPE-rotated queries and keys, the rotation of q fused
+ * into the attention's loads (vllm.cpp PR #279, vision-tower commits: the tower
+ * rotates q and k before attention; width-first, 1-based positions, as in
+ * mgattn_rope2d).  k is rotated in place by the RoPE pass (mgattn_rope2d on k); q is
+ * read-only and each workgroup rotates its query rows in registers as it loads them,
+ * rounding exactly as mgattn_rope2d does, so `out` equals, bit for bit, that of
+ * mgattn_rope2d on q and on k followed by mgattn_dense_strided -- with one read and
+ * one write of q fewer.  The images of (grids, n_img) in token order `win` (0: raster,
+ * > 0: window order, as mgattn_rope2d) must hold exactly the call's tokens
+ * (cu_seqlens[n_seg]), else MGATTN_ERR_GRID.  The fused path is the tower's: bf16 and
+ * head_dim 96; other (dtype, d) are refused (MGATTN_ERR_DTYPE, MGATTN_ERR_HEAD_DIM)
+ * before anything is launched -- use mgattn_rope2d and mgattn_dense_strided.  Other
+ * arguments, refusals and ownership as mgattn_dense_strided and mgattn_rope2d. */
+int mgattn_dense_rope2d(const void* q, void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
+                        int64_t ldo, const int32_t* cu_seqlens, int n_seg, int H, int d, float scale, int causal,
+                        int dtype, const int32_t* grids, int n_img, int win, float theta, void* stream);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int mgattn_version(void);
 

@@ -62,6 +62,18 @@ static std::string check(const Model& m) {
   std::vector<std::vector<int>> done(W, std::vector<int>(NO, INF)), issued(W, std::vector<int>(NO, -1));
   std::vector<std::vector<int>> reads(NO);  // epochs of all reads
   std::vector<int> barriers(W, 0);
+  std::vector<int> stored(NO, -1);        // last epoch a wave stored the object (WRITE), -1: never
+  std::vector<int> first_store(NO, 1 << 30);
+  for (int w = 0; w < W; ++w) {
+    int e = 0;
+    for (const Ev& ev : m.prog[w]) {
+      if (ev.kind == BARRIER) ++e;
+      if (ev.kind == WRITE) {
+        stored[ev.obj] = std::max(stored[ev.obj], e);
+        first_store[ev.obj] = std::min(first_store[ev.obj], e);
+      }
+    }
+  }
   struct Write { int w, obj, epoch; bool dma; };
   std::vector<Write> writes;
   for (int w = 0; w < W; ++w) {
@@ -94,7 +106,11 @@ static std::string check(const Model& m) {
         case READ: reads[ev.obj].push_back(e); break;
         case WRITE: writes.push_back({w, ev.obj, e, false}); break;
       }
-      if (ev.kind == READ) {
+      if (ev.kind == READ && stored[ev.obj] >= 0) {  // stored by waves: a barrier must follow every store
+        if (!(stored[ev.obj] < e))
+          return "wave " + std::to_string(w) + " reads " + m.name[ev.obj] + " in epoch " + std::to_string(e) +
+                 " before every wave's store of it is published";
+      } else if (ev.kind == READ) {
         for (int v = 0; v < W; ++v)
           if (issued[v][ev.obj] >= 0 && !(done[v][ev.obj] < e))
             return "wave " + std::to_string(w) + " reads " + m.name[ev.obj] + " in epoch " + std::to_string(e) +
@@ -113,10 +129,11 @@ static std::string check(const Model& m) {
   for (const Write& wr : writes) {
     for (int o = 0; o < NO; ++o) {
       if (o == wr.obj || !overlap(m.region[o], m.region[wr.obj])) continue;
-      int first_issue = INF;
+      int first_issue = first_store[o];  // an object stored by the waves is present from its first store
       for (int v = 0; v < W; ++v)
         if (issued[v][o] >= 0) first_issue = std::min(first_issue, issued[v][o]);
       if (first_issue > wr.epoch) continue;  // a later occupant
+      if (!wr.dma && first_issue == wr.epoch) continue;  // stores of one epoch to distinct objects
       if (wr.dma && first_issue == wr.epoch) {
         // two DMAs into overlapping regions issued in the same epoch
         if (o < wr.obj) return m.name[wr.obj] + " and " + m.name[o] + " are loaded into overlapping LDS in one epoch";
@@ -138,7 +155,7 @@ static std::string check(const Model& m) {
 
 // ---- the pipelined kernel (attn_fwd_bf16_pipe<D, W>)
 template <int D>
-static std::string pipe_case(int W, int kend) {
+static std::string pipe_case(int W, int kend, bool rope = false) {
   using G = Geometry<D>;
   const int BM = 32 * W, BN = G::kBlockN, SK = G::kStepKeys, S = G::kStages;
   const long SE = G::kStageElems, KE = G::kKElems;
@@ -152,6 +169,9 @@ static std::string pipe_case(int W, int kend) {
   }
   std::vector<int> O(W);
   for (int w = 0; w < W; ++w) O[w] = m.obj("O" + std::to_string(w), w * 32L * (D + 8), (w + 1) * 32L * (D + 8));
+  // the RoPE table's bounding boxes and angles (elements of stage 1)
+  const int box = m.obj("RoPE boxes", SE + KE, SE + KE + 2L * 4 * W);
+  const int table = m.obj("RoPE table", SE + KE + 2L * 4 * W, 2 * SE);
   m.prog.resize(W);
   for (int w = 0; w < W; ++w) {
     auto& p = m.prog[w];
@@ -162,9 +182,26 @@ static std::string pipe_case(int W, int kend) {
     };
     p.push_back({ISSUE, q, G::q_dma(BM) / W});
     issue_tile(0);
-    if (ntiles > 1 && kPipePrologueTiles >= 2) issue_tile(1);
-    p.push_back({WAIT_LEAVE, -1, vd + (ntiles > 1 ? kd + vd : 0) + (mutated("pipe_prologue_short") ? 1 : 0)});
-    p.push_back({BARRIER, -1, 0});
+    if (!rope) {
+      if (ntiles > 1 && kPipePrologueTiles >= 2) issue_tile(1);
+      p.push_back({WAIT_LEAVE, -1, vd + (ntiles > 1 ? kd + vd : 0) + (mutated("pipe_prologue_short") ? 1 : 0)});
+      p.push_back({BARRIER, -1, 0});
+    } else {
+      // RoPE of Q on load: K of tile 1 goes out with tile 0; the bounding boxes and the
+      // angle table use stage 1's V region, which receives V of tile 1 afterwards
+      if (ntiles > 1) p.push_back({ISSUE, K[1], kd});
+      p.push_back({WRITE, box, 0});
+      p.push_back({BARRIER, -1, 0});
+      p.push_back({READ, box, 0});
+      p.push_back({WRITE, table, 0});
+      if (!mutated("rope_table_no_barrier")) p.push_back({BARRIER, -1, 0});
+      p.push_back({READ, table, 0});
+      p.push_back({WAIT_LEAVE, -1, vd + (ntiles > 1 ? kd : 0)});
+      if (mutated("rope_tile1_early") && ntiles > 1) p.push_back({ISSUE, V[1], vd});
+      p.push_back({BARRIER, -1, 0});
+      if (!mutated("rope_tile1_early") && ntiles > 1) p.push_back({ISSUE, V[1], vd});
+      if (mutated("rope_table_no_barrier")) p.push_back({BARRIER, -1, 0});
+    }
     p.push_back({READ, q, 0});
     p.push_back({READ, K[0], 0});  // QK of step 0
     if (nsteps > 1) p.push_back({READ, K[pipe_k_step(0) * SK / BN], 0});
@@ -280,6 +317,8 @@ int main(int argc, char** argv) {
     const char* what = "";
     if ((r = pipe_case<96>(8, kend)).size()) what = "pipe<96, 8>";
     else if ((r = pipe_case<96>(4, kend)).size()) what = "pipe<96, 4>";
+    else if ((r = pipe_case<96>(8, kend, true)).size()) what = "pipe<96, 8, rope>";
+    else if ((r = pipe_case<96>(4, kend, true)).size()) what = "pipe<96, 4, rope>";
     else if ((r = phased_case<64>(kend)).size()) what = "phased<64>";
     else if ((r = phased_case<96>(kend)).size()) what = "phased<96>";
     else if ((r = phased_case<128>(kend)).size()) what = "phased<128>";
@@ -287,7 +326,7 @@ int main(int argc, char** argv) {
       printf("violation: %s, %d keys: %s\n", what, kend, r.c_str());
       return 1;
     }
-    cases += 5;
+    cases += 7;
   }
   printf("ok %ld\n", cases);
   return 0;

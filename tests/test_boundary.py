@@ -328,3 +328,24 @@ def test_attention_kv_ws_refusals(lib, ws, nbytes, kw, status):
     st = mg.mgattn_attention_kv_ws(Q, K, V, o, Hq * d, Hkv * d, Hkv * d, Hq * d, list(cq), list(ck), len(cq) - 1, Hq,
                                    Hkv, d, 0.1, a["window"], 1, ws, nbytes, None, check=False)
     assert st == status
+
+
+def test_dense_rope2d_refusals(lib):
+    """The fused RoPE path is bf16 at head_dim 96; the images must hold the call's
+    tokens; checks run before anything is launched (no GPU here)."""
+    base = 1 << 20
+    q, k, v, o = base, base + (1 << 24), base + (2 << 24), base + (3 << 24)
+    row = 16 * 96
+
+    def call(d=96, dtype=1, grids=((8, 8),), cu=(0, 64), win=4, theta=10000.0, H=16):
+        r = H * d
+        return mg.mgattn_dense_rope2d(q, k, v, o, r, r, r, r, list(cu), len(cu) - 1, H, d, 0.1, 0, dtype,
+                                      list(grids), win, theta, None, check=False)
+    assert call(dtype=0) == -2
+    assert call(d=64) == -3
+    assert call(d=80) == -3
+    assert call(cu=(0, 63)) == -14       # the images hold 64 tokens
+    assert call(grids=((8, 8), (2, 3)), cu=(0, 64)) == -14
+    assert call(win=-1) == -14
+    assert call(theta=1.0) == -9
+    assert call(cu=(0, 70, 64)) == -5

@@ -1,7 +1,8 @@
 """The LDS staging of the bf16 kernels is race-free (host model, no GPU).
 
 tests/lds_schedule_model.cpp replays every wave's program of the pipelined dense
-kernel (8 and 4 waves, head_dim 96) and of the phased kernel (head_dim 64, 96 and
+kernel (8 and 4 waves, head_dim 96, with and without the RoPE angle table of its
+prologue) and of the phased kernel (head_dim 64, 96 and
 128) for every key count 1..1100 and several long ones, using the schedule functions
 the kernels call (vit_perception_encoder_amd/csrc/schedule.hpp), and checks that no
 LDS region is read before its DMA is waited for and published by a barrier, none is
@@ -42,6 +43,8 @@ def test_kernel_schedules_are_race_free(model):
     "pipe_prologue_short",         # the prologue waits for one DMA too few
     "phased_issue_early",          # a stage refilled two phases early
     "phased_wait_late",            # a tile waited for two phases late
+    "rope_table_no_barrier",       # the RoPE angle table read before every wave stored it
+    "rope_tile1_early",            # tile 1's DMA over the angle table other waves still read
 ])
 def test_planted_schedule_mistakes_are_caught(model, mutation):
     r = subprocess.run([str(model), mutation], capture_output=True, text=True)

@@ -49,6 +49,7 @@
 
 #include "plan.hpp"
 #include "schedule.hpp"
+#include "window_rope.hpp"
 
 namespace mgattn {
 
@@ -73,7 +74,15 @@ struct KernelArgs {
   int32_t nsplit;     // one-token decoding: workgroups per (sequence, key/value head)
   float* part;        // nsplit > 1: partial results of the key splits (caller's workspace)
   SegTable table;
+  // 2D RoPE of Q on load (mgattn_dense_rope2d): batch tokens in raster or window order
+  // over the images of tb, pair frequencies inv_freq[i] = theta^(-4i/d)
+  struct {
+    int32_t win;
+    float inv_freq[32];
+    ImageTable tb;
+  } rope;
 };
+static_assert(sizeof(KernelArgs) <= 4096, "kernel arguments must stay within 4 KB");
 
 template <int D>
 struct Bf16Tile : sched::Geometry<D> {

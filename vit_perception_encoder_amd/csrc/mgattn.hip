@@ -229,7 +229,8 @@ bool is_decode(const int32_t* cu, int n_seg, int H, int Hkv, bool pack) {
 // Validation, plan and launches shared by every attention entry point.
 int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
            int64_t ldo, const int32_t* cu, const int32_t* cuk, int n_seg, int H, int Hkv, int d, float scale,
-           int causal, int window, int dtype, void* stream, void* ws = nullptr, size_t ws_bytes = 0) {
+           int causal, int window, int dtype, void* stream, void* ws = nullptr, size_t ws_bytes = 0,
+           const KernelArgs* rope = nullptr) {
   const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu, cuk, n_seg, H, Hkv, d, scale, causal, window, dtype);
   if (st != MGATTN_OK) return st;
   // The general bf16 kernel packs the query heads of a key/value head into one tile's
@@ -261,6 +262,7 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   // keys at exp2(-inf) = 0.
   args.c = scale == 0.0f ? 1.0f : static_cast<float>(fabs(static_cast<double>(scale)) * 1.4426950408889634);
   args.qsign = scale > 0.0f ? 1 : (scale < 0.0f ? -1 : 0);
+  if (rope) args.rope = rope->rope;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // One-token decoding (every sequence has a single new query): the key-split decode
   // kernel, nsplit workgroups per (sequence, key/value head); nsplit > 1 only with a
@@ -296,6 +298,10 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
                        : launch_all(attn_fwd_bf16<64, false>, Bf16Tile<64>::kThreads, plan, args, s);
       case 96:
         if (general) return launch_all(attn_fwd_bf16<96, true>, Bf16Tile<96>::kThreads, plan, args, s);
+        if (rope) {
+          if (bm == 128) return launch_all(attn_fwd_bf16_pipe<96, 4, true>, 4 * 64, plan, args, s);
+          return launch_all(attn_fwd_bf16_pipe<96, 8, true>, 8 * 64, plan, args, s);
+        }
         if (bm == 128) return launch_all(attn_fwd_bf16_pipe<96, 4>, 4 * 64, plan, args, s);
         return launch_all(attn_fwd_bf16_pipe<96, 8>, 8 * 64, plan, args, s);
       case 128:
@@ -607,6 +613,33 @@ int mgattn_rope2d(void* x, int64_t ldx, const int32_t* grids, int n_img, int win
   return hipLaunchKernel(kern, dim3(grid), dim3(256), params, 0, static_cast<hipStream_t>(stream)) == hipSuccess
              ? MGATTN_OK
              : MGATTN_ERR_LAUNCH;
+}
+
+int mgattn_dense_rope2d(const void* q, void* k, const void* v, void* out, int64_t ldq, int64_t ldk, int64_t ldv,
+                        int64_t ldo, const int32_t* cu_seqlens, int n_seg, int H, int d, float scale, int causal,
+                        int dtype, const int32_t* grids, int n_img, int win, float theta, void* stream) {
+  if (!dtype_ok(dtype)) return MGATTN_ERR_DTYPE;
+  if (!head_dim_ok(d)) return MGATTN_ERR_HEAD_DIM;
+  if (dtype != MGATTN_BF16) return MGATTN_ERR_DTYPE;  // the fused path is the bf16 tower's
+  if (d != 96) return MGATTN_ERR_HEAD_DIM;
+  const int st = validate(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens, nullptr, n_seg, H, H, d, scale, causal, 0,
+                          dtype);
+  if (st != MGATTN_OK) return st;
+  KernelArgs r;
+  memset(&r, 0, sizeof r);
+  const int sti = make_images(grids, n_img, &r.rope.tb);
+  if (sti != MGATTN_OK) return sti;
+  if (win < 0) return MGATTN_ERR_GRID;
+  if (r.rope.tb.start[n_img] != cu_seqlens[n_seg]) return MGATTN_ERR_GRID;  // the images hold the call's tokens
+  if (!(theta > 1.0f) || !isfinite(theta)) return MGATTN_ERR_SCALE;
+  r.rope.win = win;
+  for (int i = 0; i < d / 4; ++i)
+    r.rope.inv_freq[i] = static_cast<float>(pow(static_cast<double>(theta), -4.0 * i / d));
+  // k rotated in place by the RoPE pass, then the attention rotates q as it reads it
+  const int stk = mgattn_rope2d(k, ldk, grids, n_img, win, H, d, theta, dtype, stream);
+  if (stk != MGATTN_OK) return stk;
+  return attend(q, k, v, out, ldq, ldk, ldv, ldo, cu_seqlens, nullptr, n_seg, H, H, d, scale, causal, 0, dtype,
+                stream, nullptr, 0, &r);
 }
 
 int mgattn_version(void) { return kVersion; }

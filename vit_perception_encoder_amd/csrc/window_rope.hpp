@@ -61,6 +61,33 @@ __device__ inline int window_to_raster(int p, int gh, int gw, int win) {
   return y * gw + x;
 }
 
+// Patch coordinates (0-based) of batch token t, for tokens in raster order (win == 0)
+// or in the window order of window win.
+__device__ inline void token_patch(const ImageTable& tb, int win, int t, int* row, int* col) {
+  const int img = image_of(tb, t);
+  const int p = t - tb.start[img];
+  const int gw = tb.gw[img];
+  const int r = win > 0 ? window_to_raster(p, tb.gh[img], gw, win) : p;
+  *row = r / gw;
+  *col = r % gw;
+}
+
+// Cosine and sine of one rotation pair at 1-based position pos, frequency f.
+__device__ inline void rope_angle(float pos, float f, float* c, float* s) { sincosf(pos * f, s, c); }
+
+// One rotation pair stored as two bf16 in a 32-bit word (low half the real part):
+// (re + i im) * (c + i s), rounded to bf16.  The products are written out so that every
+// kernel that rotates (the RoPE pass, the attention kernel rotating Q on load) rounds
+// the same way: fma(re, c, -(im*s)) and fma(re, s, im*c).
+__device__ inline uint32_t rope_pair_bf16(uint32_t w, float c, float s) {
+  const float re = __uint_as_float(w << 16), im = __uint_as_float(w & 0xffff0000u);
+  const float ims = im * s, imc = im * c;
+  const __bf16 a2 = static_cast<__bf16>(__builtin_fmaf(re, c, -ims));
+  const __bf16 b2 = static_cast<__bf16>(__builtin_fmaf(re, s, imc));
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a2)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) << 16);
+}
+
 // dst row p <- src row perm(p) (gather into window order), or dst row perm(p) <- src
 // row p (inverse: back to raster order).  One wave per row p: the row's partner
 // (image, window order <-> raster) is wave-uniform and computed once; the lanes copy
@@ -116,10 +143,8 @@ void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
   const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
   if (t >= n_tokens) return;
   const int lane = threadIdx.x & 63;
-  const int img = image_of(a.tb, t);
-  const int p = t - a.tb.start[img];
-  const int gw = a.tb.gw[img];
-  const int r = a.win > 0 ? window_to_raster(p, a.tb.gh[img], gw, a.win) : p;
+  int prow = 0, pcol = 0;
+  token_patch(a.tb, a.win, t, &prow, &pcol);
   const int quarter = a.d / 4;  // pairs per half of a head
   const float f_l = a.inv_freq[lane < 2 * quarter ? lane % quarter : 0];  // loaded before the data
   float c_l = 1.0f, s_l = 0.0f;
@@ -138,10 +163,8 @@ void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
       off[u] = head * a.d + pcs[u] * kPer;
       raw[u] = *reinterpret_cast<const u32x4*>(row + off[u]);
     }
-    if (j0 == 0 && lane < 2 * quarter) {  // the angles, while the first loads are in flight
-      const float pos = static_cast<float>(lane < quarter ? r % gw + 1 : r / gw + 1);
-      sincosf(pos * f_l, &s_l, &c_l);
-    }
+    if (j0 == 0 && lane < 2 * quarter)  // the angles, while the first loads are in flight
+      rope_angle(static_cast<float>(lane < quarter ? pcol + 1 : prow + 1), f_l, &c_l, &s_l);
     asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]), "v"(raw[3]));
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -155,19 +178,14 @@ void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
       uint32_t w[4] = {raw[u][0], raw[u][1], raw[u][2], raw[u][3]};
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float re = __uint_as_float(w[k] << 16), im = __uint_as_float(w[k] & 0xffff0000u);
-          const __bf16 a2 = static_cast<__bf16>(re * cs[k] - im * sn[k]);
-          const __bf16 b2 = static_cast<__bf16>(re * sn[k] + im * cs[k]);
-          w[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a2)) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) << 16);
-        }
+        for (int k = 0; k < 4; ++k) w[k] = rope_pair_bf16(w[k], cs[k], sn[k]);
       } else {
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const float re = __uint_as_float(w[2 * k]), im = __uint_as_float(w[2 * k + 1]);
-          w[2 * k] = __float_as_uint(re * cs[k] - im * sn[k]);
-          w[2 * k + 1] = __float_as_uint(re * sn[k] + im * cs[k]);
+          const float ims = im * sn[k], imc = im * cs[k];
+          w[2 * k] = __float_as_uint(__builtin_fmaf(re, cs[k], -ims));
+          w[2 * k + 1] = __float_as_uint(__builtin_fmaf(re, sn[k], imc));
         }
       }
       if (j0 + u * 64 + lane < total) *reinterpret_cast<u32x4*>(row + off[u]) = u32x4{w[0], w[1], w[2], w[3]};

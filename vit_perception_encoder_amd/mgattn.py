@@ -30,7 +30,7 @@ EXPORTS = ["mgattn_dense", "mgattn_dense_strided", "mgattn_attention_kv", "mgatt
            "mgattn_attention_kv_noalloc", "mgattn_attention_kv_noalloc_scratch_bytes",
            "mgattn_attention_kv_workspace", "mgattn_strerror", "mgattn_dense_supported", "mgattn_dense_lds_bytes",
            "mgattn_dense_block_m", "mgattn_dense_plan_block_m", "mgattn_dense_plan", "mgattn_dense_tile", "mgattn_window_segments",
-           "mgattn_window_permute", "mgattn_rope2d", "mgattn_version"]
+           "mgattn_window_permute", "mgattn_rope2d", "mgattn_dense_rope2d", "mgattn_version"]
 
 
 class MgattnError(RuntimeError):
@@ -91,6 +91,9 @@ def load_library(path: str | os.PathLike | None = None):
     lib.mgattn_window_permute.argtypes = [vp, vp, i64, vp, i32, i32, i32, vp]
     lib.mgattn_rope2d.restype = i32
     lib.mgattn_rope2d.argtypes = [vp, i64, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.mgattn_dense_rope2d.restype = i32
+    lib.mgattn_dense_rope2d.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, vp, i32, i32, i32, f32, i32, i32, vp, i32,
+                                        i32, f32, vp]
     lib.mgattn_version.restype = i32
     lib.mgattn_version.argtypes = []
     if path is None:
@@ -383,6 +386,30 @@ def mgattn_rope2d(x, ldx: int, grids, win: int, H: int, d: int, theta: float, dt
                            float(theta), int(dtype), _stream(stream))
     if check and st != 0:
         raise MgattnError(st, "mgattn_rope2d")
+    return st
+
+
+def mgattn_dense_rope2d(q, k, v, out, ldq: int, ldk: int, ldv: int, ldo: int, cu_seqlens: Sequence[int], n_seg: int,
+                        H: int, d: int, scale: float, causal: int, dtype: int, grids, win: int, theta: float,
+                        stream=None, check: bool = True) -> int:
+    """Attention over 2D-RoPE-rotated q and k, q rotated on load, k rotated in place
+    (see mgattn_dense_rope2d in include/mgattn.h)."""
+    lib = load_library()
+    cu, ncu = _cu_array(cu_seqlens)
+    if ncu < n_seg + 1:
+        raise ValueError(f"cu_seqlens has {ncu} entries, n_seg={n_seg} needs {n_seg + 1}")
+    eb = _ELEM_BYTES.get(int(dtype))
+    if eb is not None and n_seg >= 0:
+        T = int(cu[n_seg])
+        for name, t, ld in (("q", q, ldq), ("k", k, ldk), ("v", v, ldv), ("out", out, ldo)):
+            _check_tensor(name, t, eb, _span(T, int(ld), H * d, eb))
+    g, n_img = _grid_array(grids)
+    st = lib.mgattn_dense_rope2d(_ptr(q), _ptr(k), _ptr(v), _ptr(out), int(ldq), int(ldk), int(ldv), int(ldo),
+                                 ctypes.cast(cu, ctypes.c_void_p), int(n_seg), int(H), int(d), float(scale), int(causal),
+                                 int(dtype), ctypes.cast(g, ctypes.c_void_p), n_img, int(win), float(theta),
+                                 _stream(stream))
+    if check and st != 0:
+        raise MgattnError(st, "mgattn_dense_rope2d")
     return st
 
 
