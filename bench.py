@@ -40,7 +40,7 @@ METRIC = "attention TFLOP/s (%bf16 MFMA peak) + ms per 50-layer tower attn @4096
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published 2.5 PFLOP/s): 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published 8 TB/s)
 THETA = 10000.0
-KERNEL_NAME = "attn_fwd_bf16_pipe<96, 8>"  # the dense head_dim-96 kernel the tower's layers launch
+KERNEL_NAME = "attn_fwd_bf16_pipe<96, 8, false, false>"  # the dense head_dim-96 kernel the tower's layers launch (W, rope, key split)
 TRAFFIC_FILE = ROOT / "profiles" / "attn_fwd_bf16_pipe_96_tower4096_traffic.json"
 KERNEL_SOURCES = ["vit_perception_encoder_amd/csrc/attn_bf16_pipe.hpp", "vit_perception_encoder_amd/csrc/attn_bf16.hpp",
                   "vit_perception_encoder_amd/csrc/schedule.hpp", "vit_perception_encoder_amd/csrc/plan.hpp",
@@ -144,6 +144,87 @@ def time_launches(torch, fn, reps: int = 30, warm: int = 10) -> float:
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
+def time_graph(torch, fn, n: int = 20, reps: int = 10) -> float:
+    """Milliseconds per call of fn(stream) with n calls captured into one HIP graph and
+    replayed: the kernels' own duration plus the gaps between graph nodes, without the
+    host launch overhead that events around a single launch include (several us,
+    comparable to a short HBM-bound kernel).  Best of `reps` replays after >= 5 ms of
+    warm-up."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for _ in range(n):
+            fn(cap)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 5e-3:
+        graph.replay()
+        torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / n)
+    return best
+
+
+def tower_448(torch, mg, wl, reps: int = 10) -> dict:
+    """The 448x448 image's tower: every one of its 50 layers attends one 1024-token
+    segment (a single 32x32 window).  50 layers of seeded N(0,1) bf16 inputs resident on
+    the device, the 50 launches captured into one graph and replayed; milliseconds per
+    replay (best of `reps`) and the TFLOP/s of the 50 launches."""
+    dev = torch.device("cuda:0")
+    T, H, d = 1024, wl.HEADS, wl.HEAD_DIM
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(448)
+    layers = [tuple(torch.randn(T, H * d, generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+              for _ in range(wl.N_LAYERS)]
+    out = torch.empty(T, H * d, dtype=torch.bfloat16, device=dev)
+    cu = [0, T]
+
+    def run(strm):
+        for q, k, v in layers:
+            mg.mgattn_dense(q, k, v, out, cu, 1, H, d, wl.SCALE, 0, mg.MGATTN_BF16, strm)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            run(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 5e-3:
+        graph.replay()
+        torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    flops = wl.N_LAYERS * 4.0 * T * T * d * H
+    return {"ms": best, "layers": wl.N_LAYERS, "us_per_layer": best * 1e3 / wl.N_LAYERS,
+            "block_m": mg.mgattn_dense_plan_block_m(cu, 1, H, d, mg.MGATTN_BF16, 0),
+            "tflops": flops / (best * 1e-3) / 1e12, "frac": flops / (best * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def config_times(torch, mg, wl):
     """Each parity workload timed on its own (events around each launch, median): the
     f32 256-token segment, the 1024-token full layer, the 4 x 1024 window layer, and the
@@ -229,21 +310,32 @@ def token_path(torch, mg, wl, layers):
                 bt[name] = min(bt[name], time_launches(torch, fn))
         res[f"rope_attention_{lname}"] = {"unfused_ms": bt["unfused"], "fused_ms": bt["fused"],
                                           "fused_tflops": fl_l / (bt["fused"] * 1e-3) / 1e12}
+    # the HBM-bound kernels: "ms" from a graph of 20 calls (per call), "ms_events" with
+    # events around single launches (host launch overhead included)
     for name, grids in (("tower_64x64", [(64, 64)]), ("ragged_17408", [(128, 96), (64, 64), (32, 32)])):
         T = sum(gh * gw for gh, gw in grids)
         x = torch.randn(T, row, device=dev).to(torch.bfloat16)
         y = torch.empty_like(x)
-        ms_g = time_launches(torch, lambda: mg.mgattn_window_permute(x, y, row * 2, grids, 32, 0, stream))
+
+        def gather(s):
+            mg.mgattn_window_permute(x, y, row * 2, grids, 32, 0, s)
+
+        ms_g = time_graph(torch, gather)
+        ms_ge = time_launches(torch, lambda: gather(stream))
         moved = 2 * T * row * 2  # read + write
         qkv3 = torch.randn(T, 3 * row, device=dev).to(torch.bfloat16)
 
-        # q and k are adjacent in a merged qkv row: one call over their 2H heads
-        ms_r = time_launches(torch, lambda: mg.mgattn_rope2d(qkv3[:, :2 * row], qkv3.stride(0), grids, 32, 2 * H, d,
-                                                            THETA, mg.MGATTN_BF16, stream))
+        def rope(s):  # q and k are adjacent in a merged qkv row: one call over their 2H heads
+            mg.mgattn_rope2d(qkv3[:, :2 * row], qkv3.stride(0), grids, 32, 2 * H, d, THETA, mg.MGATTN_BF16, s)
+
+        ms_r = time_graph(torch, rope)
+        ms_re = time_launches(torch, lambda: rope(stream))
         rot = 2 * 2 * T * row * 2  # q and k, read + write
-        res[f"window_gather_{name}"] = {"ms": ms_g, "bytes": moved, "gbs": moved / (ms_g * 1e-3) / 1e9,
+        res[f"window_gather_{name}"] = {"ms": ms_g, "ms_events": ms_ge, "bytes": moved,
+                                        "gbs": moved / (ms_g * 1e-3) / 1e9,
                                         "frac_hbm": moved / (ms_g * 1e-3) / 1e9 / PEAK_HBM_GBS}
-        res[f"rope2d_qk_{name}"] = {"ms": ms_r, "launches": 1, "bytes": rot, "gbs": rot / (ms_r * 1e-3) / 1e9,
+        res[f"rope2d_qk_{name}"] = {"ms": ms_r, "ms_events": ms_re, "launches": 1, "bytes": rot,
+                                    "gbs": rot / (ms_r * 1e-3) / 1e9,
                                     "frac_hbm": rot / (ms_r * 1e-3) / 1e9 / PEAK_HBM_GBS}
     # text decoder attention (32 query / 2 key-value heads, head size 128, window 2048)
     Hq, Hkv, dt, W = 32, 2, 128, 2048
@@ -271,14 +363,21 @@ def token_path(torch, mg, wl, layers):
     # in a workspace (decode kernel + merge kernel), and one workgroup per pair without it
     wsb = mg.mgattn_attention_kv_workspace(cq, ck, B, Hq, Hkv, dt, W, mg.MGATTN_BF16)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    ms = time_launches(torch, lambda: mg.mgattn_attention_kv_ws(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt,
-                                                               cq, ck, B, Hq, Hkv, dt, dt ** -0.5, W, mg.MGATTN_BF16,
-                                                               ws, wsb, stream))
-    res["text_decode_32x4096_window2048"] = {"ms": ms, "kv_bytes": kv_bytes, "gbs": kv_bytes / (ms * 1e-3) / 1e9,
+    def decode_ws(s):
+        mg.mgattn_attention_kv_ws(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt, cq, ck, B, Hq, Hkv, dt,
+                                  dt ** -0.5, W, mg.MGATTN_BF16, ws, wsb, s)
+
+    def decode_plain(s):
+        mg.mgattn_attention_kv(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt, cq, ck, B, Hq, Hkv, dt,
+                               dt ** -0.5, W, mg.MGATTN_BF16, s)
+
+    ms = time_graph(torch, decode_ws)
+    ms_e = time_launches(torch, lambda: decode_ws(stream))
+    res["text_decode_32x4096_window2048"] = {"ms": ms, "ms_events": ms_e, "kv_bytes": kv_bytes,
+                                             "gbs": kv_bytes / (ms * 1e-3) / 1e9,
                                              "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                              "workspace_bytes": wsb, "launches": 2 if wsb else 1}
-    ms = time_launches(torch, lambda: mg.mgattn_attention_kv(qd, kc, vc, od, Hq * dt, Hkv * dt, Hkv * dt, Hq * dt, cq,
-                                                            ck, B, Hq, Hkv, dt, dt ** -0.5, W, mg.MGATTN_BF16, stream))
+    ms = time_graph(torch, decode_plain)
     res["text_decode_32x4096_window2048_no_workspace"] = {"ms": ms, "kv_bytes": kv_bytes,
                                                           "gbs": kv_bytes / (ms * 1e-3) / 1e9,
                                                           "frac_hbm": kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -484,6 +583,7 @@ def main() -> int:
           flush=True)
     token = None if args.no_token_path else token_path(torch, mg, wl, layers)
     configs = None if args.no_token_path else config_times(torch, mg, wl)
+    t448 = None if args.no_token_path else tower_448(torch, mg, wl)
 
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
@@ -540,6 +640,7 @@ def main() -> int:
             "oracle_parity_full_layers_max_abs_err": parity,
             "token_path": token,
             "configs": configs,
+            "tower_448": t448,
             "kernel_source_sha256": kernel_source_hash(),
         },
     }

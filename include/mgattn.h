@@ -218,7 +218,8 @@ int mgattn_dense_supported(int H, int d, int dtype);
 
 /* Bytes of LDS (on-chip shared memory) one workgroup of the (d, dtype) kernel asks
  * for, or a negative mgattn_status if (d, dtype) is not supported.  Pure host
- * arithmetic, no GPU needed; equals the static LDS footprint of the kernel. */
+ * arithmetic, no GPU needed; equals the static LDS footprint of the kernel (for bf16
+ * head_dim 96, of its largest workgroup shape: the key-split shapes use less). */
 long mgattn_dense_lds_bytes(int d, int dtype);
 
 /* Queries per workgroup of the (d, dtype) kernel (the tallest q-tile it uses), or a
@@ -228,9 +229,11 @@ int mgattn_dense_block_m(int d, int dtype);
 /* Queries per workgroup mgattn_dense uses for this segment table (same arguments and
  * refusals as mgattn_dense_plan), or a negative mgattn_status.  Pure host arithmetic.
  * The bf16 head_dim-96 kernel takes 256 when the (segment, head, q-tile) units of 256
- * give at least 256 workgroups (one per CU), else 128, so a short call (one
- * 1024-token segment of 16 heads: 64 units of 256, 128 of 128) spreads over more CUs;
- * every other (d, dtype) has the single height of mgattn_dense_block_m. */
+ * give at least 256 workgroups (one per CU).  Otherwise a non-causal call splits each
+ * tile's keys between two wave groups and takes 128 if the units of 128 give 256
+ * workgroups, else 64 (one 1024-token segment of 16 heads: 64 units of 256, 256 of
+ * 64); a causal call takes 128.  Every other (d, dtype) has the single height of
+ * mgattn_dense_block_m. */
 int mgattn_dense_plan_block_m(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal);
 
 /* Introspection of the work split (pure host arithmetic, no GPU needed).

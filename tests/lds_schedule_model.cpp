@@ -161,7 +161,8 @@ static std::string pipe_case(int W, int kend, bool rope = false) {
   const long SE = G::kStageElems, KE = G::kKElems;
   const int ntiles = (kend + BN - 1) / BN, nsteps = (kend + SK - 1) / SK;
   Model m;
-  const int q = m.obj("Q", (S - 1) * SE, (S - 1) * SE + static_cast<long>(BM) * D);
+  const int q = m.obj("Q", pipe_q_elem<D>(), pipe_q_elem<D>() + G::q_pad_elems(BM));
+  if (pipe_q_elem<D>() + G::q_pad_elems(BM) > pipe_lds_elems<D>(BM)) return "Q tile outside the LDS";
   std::vector<int> K(ntiles), V(ntiles);
   for (int t = 0; t < ntiles; ++t) {
     K[t] = m.obj("K" + std::to_string(t), (t % S) * SE, (t % S) * SE + KE);
@@ -180,7 +181,7 @@ static std::string pipe_case(int W, int kend, bool rope = false) {
       p.push_back({ISSUE, K[t], kd});
       p.push_back({ISSUE, V[t], vd});
     };
-    p.push_back({ISSUE, q, G::q_dma(BM) / W});
+    p.push_back({ISSUE, q, G::q_pad_dma_of(w, W, BM)});
     issue_tile(0);
     if (!rope) {
       if (ntiles > 1 && kPipePrologueTiles >= 2) issue_tile(1);
@@ -218,6 +219,75 @@ static std::string pipe_case(int W, int kend, bool rope = false) {
     }
     if (!mutated("pipe_no_final_barrier")) p.push_back({BARRIER, -1, 0});
     p.push_back({WRITE, O[w], 0});
+  }
+  return check(m);
+}
+
+// ---- the key-split pipelined kernel (attn_fwd_bf16_pipe<D, W, rope, true>): two wave
+// groups of W/2 waves, each wave one step (half a tile) per iteration; K and V rings
+template <int D>
+static std::string split_case(int W, int kend, bool rope = false) {
+  using G = SplitGeometry<D>;
+  const int QB = W / 2, BM = 32 * QB, BN = G::kBlockN;
+  const long KE = G::kKElems, VE = G::kVElems, OP = D + 8;
+  const int ntiles = (kend + BN - 1) / BN, nsteps = ntiles;
+  Model m;
+  const int q = m.obj("Q", G::kQElem, G::kQElem + G::q_pad_elems(BM));
+  if (G::kQElem + G::q_pad_elems(BM) > G::lds_elems(BM) || G::lds_elems(BM) * 2 > 160 * 1024)
+    return "Q tile outside the LDS";
+  std::vector<int> K(ntiles), V(ntiles);
+  for (int t = 0; t < ntiles; ++t) {
+    K[t] = m.obj("K" + std::to_string(t), G::k_slot_elem(t), G::k_slot_elem(t) + KE);
+    V[t] = m.obj("V" + std::to_string(t), G::v_slot_elem(t), G::v_slot_elem(t) + VE);
+  }
+  // group 0's output staging rows, then group 1's partial results (13 x 64 x 16 bytes per wave)
+  std::vector<int> O(QB), P(QB);
+  const long part0 = QB * 32L * OP, part_elems = 13L * 64 * 8;
+  for (int b = 0; b < QB; ++b) {
+    O[b] = m.obj("O" + std::to_string(b), b * 32L * OP, (b + 1) * 32L * OP);
+    P[b] = m.obj("partial" + std::to_string(b), part0 + b * part_elems, part0 + (b + 1) * part_elems);
+  }
+  const long tab0 = G::v_slot_elem(2);
+  const int box = m.obj("RoPE boxes", tab0, tab0 + 2L * 4 * W);
+  const int table = m.obj("RoPE table", tab0 + 2L * 4 * W, tab0 + VE);
+  m.prog.resize(W);
+  for (int w = 0; w < W; ++w) {
+    auto& p = m.prog[w];
+    const int grp = w / QB, qb = w % QB;
+    const int kd = G::k_dma_of(w, W), vd = G::v_dma_of(w, W);
+    p.push_back({ISSUE, q, G::q_pad_dma_of(w, W, BM)});
+    p.push_back({ISSUE, K[0], kd});
+    if (ntiles > 1) p.push_back({ISSUE, K[1], kd});
+    p.push_back({ISSUE, V[0], vd});
+    if (rope) {
+      p.push_back({WRITE, box, 0});
+      p.push_back({BARRIER, -1, 0});
+      p.push_back({READ, box, 0});
+      p.push_back({WRITE, table, 0});
+      p.push_back({BARRIER, -1, 0});
+      p.push_back({READ, table, 0});
+    }
+    p.push_back({WAIT_LEAVE, -1, vd + (ntiles > 1 ? kd : 0)});
+    p.push_back({BARRIER, -1, 0});
+    p.push_back({READ, q, 0});
+    p.push_back({READ, K[0], 0});  // QK of step 0
+    for (int j = 0; j <= nsteps; ++j) {
+      p.push_back({WAIT_LEAVE, -1, (j < ntiles ? vd : 0) + (mutated("split_leave_k") ? kd : 0)});
+      p.push_back({BARRIER, -1, 0});
+      const int tk = split_issue_k(j) + (mutated("split_k_early") ? 1 : 0), tv = split_issue_v(j);
+      if (tk < ntiles) p.push_back({ISSUE, K[tk], kd});
+      if (tv < ntiles) p.push_back({ISSUE, V[tv], vd});
+      if (j + 1 < nsteps) p.push_back({READ, K[split_k_tile(j)], 0});
+      if (j >= 1) p.push_back({READ, V[split_v_tile(j)], 0});
+    }
+    p.push_back({BARRIER, -1, 0});
+    if (grp == 1) p.push_back({WRITE, P[qb], 0});
+    if (!mutated("split_merge_no_barrier")) p.push_back({BARRIER, -1, 0});
+    if (grp == 0) {
+      p.push_back({READ, P[qb], 0});
+      p.push_back({WRITE, O[qb], 0});
+    }
+    if (mutated("split_merge_no_barrier")) p.push_back({BARRIER, -1, 0});
   }
   return check(m);
 }
@@ -319,6 +389,10 @@ int main(int argc, char** argv) {
     else if ((r = pipe_case<96>(4, kend)).size()) what = "pipe<96, 4>";
     else if ((r = pipe_case<96>(8, kend, true)).size()) what = "pipe<96, 8, rope>";
     else if ((r = pipe_case<96>(4, kend, true)).size()) what = "pipe<96, 4, rope>";
+    else if ((r = split_case<96>(8, kend)).size()) what = "pipe<96, 8, split>";
+    else if ((r = split_case<96>(4, kend)).size()) what = "pipe<96, 4, split>";
+    else if ((r = split_case<96>(8, kend, true)).size()) what = "pipe<96, 8, rope, split>";
+    else if ((r = split_case<96>(4, kend, true)).size()) what = "pipe<96, 4, rope, split>";
     else if ((r = phased_case<64>(kend)).size()) what = "phased<64>";
     else if ((r = phased_case<96>(kend)).size()) what = "phased<96>";
     else if ((r = phased_case<128>(kend)).size()) what = "phased<128>";
@@ -326,7 +400,7 @@ int main(int argc, char** argv) {
       printf("violation: %s, %d keys: %s\n", what, kend, r.c_str());
       return 1;
     }
-    cases += 7;
+    cases += 11;
   }
   printf("ok %ld\n", cases);
   return 0;

@@ -53,17 +53,19 @@ def test_supported_domain(lib):
 def test_lds_bytes_arithmetic(lib):
     """The LDS a workgroup asks for.  bf16: S stages of a 128-key K tile (pitch d+8)
     and a row-major 128-key V tile (pitch d), S = 3 when three stages fit the 160 KiB
-    of one CU, else 2.  f32: two stages of 32-key K and V tiles (pitch d+4).  The
-    bound is inclusive: d=96 bf16 asks for 153,600 bytes, inside 163,840."""
+    of one CU, else 2; at d=96 (the pipelined kernel) the 256-row Q tile, padded to
+    pitch d+8, starts at the third stage and runs past it.  f32: two stages of 32-key K
+    and V tiles (pitch d+4).  The bound is inclusive: d=96 bf16 asks for 155,648 bytes,
+    inside 163,840."""
     for d in (64, 96, 128):
         stage = (128 * (d + 8) + 128 * d) * 2
         stages = 3 if 3 * stage <= 160 * 1024 else 2
-        want_bf16 = stages * stage
+        want_bf16 = stages * stage if d != 96 else max(3 * stage, 2 * stage + 256 * (d + 8) * 2)
         want_f32 = 2 * 2 * 32 * (d + 4) * 4
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_BF16) == want_bf16
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_F32) == want_f32
         assert want_bf16 <= 160 * 1024 and want_f32 <= 160 * 1024
-    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 153600
+    assert mg.mgattn_dense_lds_bytes(96, mg.MGATTN_BF16) == 155648
     assert mg.mgattn_dense_lds_bytes(128, mg.MGATTN_BF16) == 135168
     assert mg.mgattn_dense_lds_bytes(80, mg.MGATTN_BF16) == -3
     assert mg.mgattn_dense_lds_bytes(96, 7) == -2
@@ -183,20 +185,22 @@ def test_plan_is_a_bijection(lib, cu, H, dtype, causal):
     assert set(seen) == _expected_tiles(cu, H, bm)
 
 
-@pytest.mark.parametrize("cu,H,want", [
-    ([0, 4096], 16, 256),                 # the tower's full layer: 256 workgroups of 256 queries
-    ([0, 1024, 2048, 3072, 4096], 16, 256),  # its window layer
-    ([0, 1024], 16, 128),                 # one 448x448 image: 64 units of 256
-    ([0, 2048], 16, 128),                 # 128 units of 256
-    ([0, 100], 1, 128),                   # nothing fills the chip: the shorter tile
-    ([0, 1024] + [1024 + 64 * i for i in range(1, 49)], 16, 256),  # 49 segments x 16 heads
+@pytest.mark.parametrize("cu,H,want,want_causal", [
+    ([0, 4096], 16, 256, 256),            # the tower's full layer: 256 workgroups of 256 queries
+    ([0, 1024, 2048, 3072, 4096], 16, 256, 256),  # its window layer
+    ([0, 1024], 16, 64, 128),             # one 448x448 image: 64 units of 256, 256 of 64 (key-split)
+    ([0, 2048], 16, 128, 128),            # 128 units of 256, 256 of 128 (key-split)
+    ([0, 100], 1, 64, 128),               # nothing fills the chip: the shortest tile
+    ([0, 1024] + [1024 + 64 * i for i in range(1, 49)], 16, 256, 256),  # 49 segments x 16 heads
 ])
-def test_plan_block_m_fills_the_chip(lib, cu, H, want):
-    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 96, 1, 0) == want
-    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 64, 1, 0) == 256  # one tile height at d = 64
-    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, H, 96, 0, 0) == 128  # and for f32
-    assert sum(mg.mgattn_dense_plan(cu, len(cu) - 1, H, 96, 1, 0)) == H * sum(
-        -(-(cu[g + 1] - cu[g]) // want) for g in range(len(cu) - 1))
+def test_plan_block_m_fills_the_chip(lib, cu, H, want, want_causal):
+    n = len(cu) - 1
+    for causal, bm in ((0, want), (1, want_causal)):
+        assert mg.mgattn_dense_plan_block_m(cu, n, H, 96, 1, causal) == bm
+        assert mg.mgattn_dense_plan_block_m(cu, n, H, 64, 1, causal) == 256  # one tile height at d = 64
+        assert mg.mgattn_dense_plan_block_m(cu, n, H, 96, 0, causal) == 128  # and for f32
+        assert sum(mg.mgattn_dense_plan(cu, n, H, 96, 1, causal)) == H * sum(
+            -(-(cu[g + 1] - cu[g]) // bm) for g in range(n))
 
 
 def test_plan_orders_longest_first_and_splits(lib):

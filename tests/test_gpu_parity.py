@@ -133,6 +133,36 @@ def test_ragged_lengths(torch, dtype, causal):
     _full_check(torch, _rand_case(f"ragged_{dtype}_{causal}", RAGGED, H=4, dtype=dtype, causal=causal, seed=11))
 
 
+SPLIT_EDGES = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 1023, 1024, 1025]
+
+
+def test_key_split_tile_edges(torch):
+    """Launches too small to fill the chip split each tile's keys between two wave
+    groups (64 keys of every 128 each) and merge their (m, l, O): segments ending on
+    both sides of every half-tile edge, including ones where the second group sees no
+    key at all."""
+    case = _rand_case("split_edges", SPLIT_EDGES, H=2, seed=15)
+    assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, 2, 96, wl.BF16, 0) == 64
+    _full_check(torch, case)
+
+
+def test_key_split_large_logits(torch):
+    """Key-split merge with maxima far apart: keys scaled x8 (scores with a standard
+    deviation near 8), so the two groups' running maxima differ by several units and
+    each group's lazy rescaling fires on its own."""
+    case = _rand_case("split_logits", [1024, 700], H=4, seed=16, kscale=8.0)
+    assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, 4, 96, wl.BF16, 0) == 64
+    _full_check(torch, case)
+
+
+def test_key_split_128_query_tiles(torch):
+    """One 2048-token segment of 16 heads: 128 units of 256 queries, 256 of 128, so
+    128-query tiles with the keys split between two groups of four waves."""
+    case = _rand_case("split_2048", [2048], H=16, seed=17)
+    assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, 16, 96, wl.BF16, 0) == 128
+    _full_check(torch, case)
+
+
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
 def test_head_dims(torch, d, dtype):
@@ -219,16 +249,35 @@ def test_key_shift_invariance_stress(torch):
 
 
 def test_segment_independence_and_determinism(torch):
+    """A segment's output does not depend on the other segments of the call, bit for
+    bit, among calls that run the same workgroup shape.  The shape follows the call's
+    size (four 1024-token windows of 16 heads run 256-query tiles, one window alone
+    runs 64-query key-split tiles), and across shapes the sums are taken in another
+    order, so the outputs agree to rounding (each is checked against the oracle
+    elsewhere).  256-query shape: the window layer against its windows in reverse
+    order; key-split shape: four heads, each window alone against the four together."""
     case = wl.config_window896()
     say("segment independence")
-    got, _ = run(torch, case.q, case.k, case.v, case.cu_seqlens, 16, 96, case.scale, 0, wl.BF16)
-    again, _ = run(torch, case.q, case.k, case.v, case.cu_seqlens, 16, 96, case.scale, 0, wl.BF16)
+    cu = [int(x) for x in case.cu_seqlens]
+    got, _ = run(torch, case.q, case.k, case.v, cu, 16, 96, case.scale, 0, wl.BF16)
+    again, _ = run(torch, case.q, case.k, case.v, cu, 16, 96, case.scale, 0, wl.BF16)
     assert np.array_equal(got, again)
-    cu = case.cu_seqlens
+    assert mg.mgattn_dense_plan_block_m(cu, 4, 16, 96, wl.BF16, 0) == 256
+    order = [3, 2, 1, 0]
+    rq, rk, rv = (np.concatenate([x[cu[g]:cu[g + 1]] for g in order]) for x in (case.q, case.k, case.v))
+    rev, _ = run(torch, rq, rk, rv, cu, 16, 96, case.scale, 0, wl.BF16)
+    for i, g in enumerate(order):
+        assert np.array_equal(rev[cu[i]:cu[i + 1]], got[cu[g]:cu[g + 1]])
+    # four heads: every call below runs the key-split shape
+    q4, k4, v4 = (np.ascontiguousarray(x.reshape(case.T, 16, 96)[:, :4, :].reshape(case.T, 4 * 96))
+                  for x in (case.q, case.k, case.v))
+    assert mg.mgattn_dense_plan_block_m(cu, 4, 4, 96, wl.BF16, 0) == 64
+    assert mg.mgattn_dense_plan_block_m([0, 1024], 1, 4, 96, wl.BF16, 0) == 64
+    all4, _ = run(torch, q4, k4, v4, cu, 4, 96, case.scale, 0, wl.BF16)
     for g in range(4):
-        a, b = int(cu[g]), int(cu[g + 1])
-        one, _ = run(torch, case.q[a:b], case.k[a:b], case.v[a:b], [0, b - a], 16, 96, case.scale, 0, wl.BF16)
-        assert np.array_equal(one, got[a:b])
+        a, b = cu[g], cu[g + 1]
+        one, _ = run(torch, q4[a:b], k4[a:b], v4[a:b], [0, b - a], 4, 96, case.scale, 0, wl.BF16)
+        assert np.array_equal(one, all4[a:b])
 
 
 def test_runtime_refusals_on_device(torch):

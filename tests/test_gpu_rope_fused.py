@@ -73,12 +73,21 @@ def test_causal_negative_scale_merged_qkv(torch):
     _case(torch, [(24, 40), (7, 9)], 8, "full", causal=1, scale=-0.07, seed=920, merged=True)
 
 
+@pytest.mark.parametrize("grid,bm", [((32, 32), 64), ((32, 64), 128)])
+def test_key_split_shapes(torch, grid, bm):
+    """A 448x448 image (one 1024-token segment: 64-query tiles, keys split between two
+    wave groups) and a 2048-token one (128-query key-split tiles), full attention."""
+    T = grid[0] * grid[1]
+    assert mg.mgattn_dense_plan_block_m([0, T], 1, 16, 96, wl.BF16, 0) == bm
+    _case(torch, [grid], 32, "full", seed=940 + bm)
+
+
 def test_raster_order_against_oracle(torch):
-    """Tokens in raster order (win = 0), 128-query tiles (a short call); the fused
-    output against the oracle on the rotated bf16 q and k the RoPE pass stores."""
+    """Tokens in raster order (win = 0), 64-query key-split tiles (a short call); the
+    fused output against the oracle on the rotated bf16 q and k the RoPE pass stores."""
     grids = [(20, 30)]
     qr, kr, v, got, cu, scale = _case(torch, grids, 0, "full", seed=930)
-    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, 16, 96, wl.BF16, 0) == 128
+    assert mg.mgattn_dense_plan_block_m(cu, len(cu) - 1, 16, 96, wl.BF16, 0) == 64
     T = 600
     qh, kh, vh = (from_device(x, torch).astype(np.float32) for x in (qr, kr, v))
     to_bits = wl.f32_to_bf16_bits  # exact: the values are bf16 already

@@ -20,8 +20,10 @@
 // later slot and by a slice of the softmax, with a scheduling fence after each slot
 // so the compiler keeps that interleave.  Both waves of a SIMD do the same, so the
 // matrix core always has an MFMA waiting while the two VALU streams share the rest.
-// S and P are double-buffered (the MFMAs write S(j+1) and read P(j-1) while the
-// softmax reads S(j) and writes P(j)).
+// S and P have one register buffer each, shared by two steps: the QK MFMAs write
+// S(j+1) into a 32-key block only after the softmax has read S(j) from it, and the
+// softmax writes P(j) into a block only after the PV MFMAs have read P(j-1) from it
+// (both products run block-major, the softmax slices are placed to match).
 //
 // LDS: K of step s is read in iteration s-1, V of step s in iteration s+1, so tile t
 // (steps 2t, 2t+1) is live in iterations 2t-1 .. 2t+2.  One barrier per tile, at the
@@ -70,8 +72,8 @@ struct PipeTile {
   static constexpr int kNPV = kNB * 2 * kCT;         // PV MFMAs per iteration
   static constexpr int kNQK = kKS * kNB;             // QK MFMAs per iteration
   static constexpr int kNSlot = kNPV + kNQK;
-  static constexpr int kDV = 2;                      // V^T read distance (slots)
-  static constexpr int kDK = 3;                      // K read distance (slots)
+  static constexpr int kDV = 3;                      // V^T read distance (slots)
+  static constexpr int kDK = 4;                      // K read distance (slots)
   // Slots 0 .. kNPV-1: PV MFMA i = (32-key block b, 16-key half h2, channel tile ct),
   // block-major, so block 0 of P(j-1) is dead after slot kNPV/2 - 1.
   static constexpr int pv_b(int i) { return i / (2 * kCT); }
@@ -106,12 +108,21 @@ struct PipeTile {
 // rotation pairs are computed while the prologue's DMA is in flight, and the rotation
 // rounds exactly as the RoPE pass does (window_rope.hpp), so the result is that of
 // rotating q in memory first.
-template <int D, int W, bool kRope = false>
+// kSplit: the keys are split between two wave groups of W/2 waves (query tiles of
+// 16W), group g taking the second half of every 128-key tile when g = 1, each wave
+// running its own online softmax over its half; at the end group 1 hands its (m, l, O)
+// to group 0 through LDS, which merges them and stores the tile.  For launches whose
+// (segment, head, tile) units leave CUs idle: it halves the query tile and the steps
+// per wave.  Non-causal only.
+template <int D, int W, bool kRope = false, bool kSplit = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W == 8 ? 2 : 1, 2)))
 void attn_fwd_bf16_pipe(KernelArgs a) {
   using TL = Bf16Tile<D>;
   using PT = PipeTile<D>;
-  constexpr int BM = 32 * W, BN = TL::kBlockN;
+  using SG = sched::SplitGeometry<D>;
+  constexpr int G = kSplit ? 2 : 1;  // key groups
+  constexpr int QB = W / G;          // 32-query blocks
+  constexpr int BM = 32 * QB, BN = TL::kBlockN;
   constexpr int SK = TL::kStepKeys;
   constexpr int NB = PT::kNB, KS = PT::kKS, CT = PT::kCT;
   constexpr int NPV = PT::kNPV, NQK = PT::kNQK, NSLOT = PT::kNSlot;
@@ -123,7 +134,17 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   constexpr int VDMA_W = (VDMA + W - 1) / W;
   constexpr float kRescaleLog2 = 8.0f;
 
-  __shared__ __attribute__((aligned(16))) __bf16 lds[TL::kStages * TL::kStageElems];
+  constexpr int KE = TL::kKElems;
+  // Q rows are padded like K rows, so the Q fragment reads are free of bank conflicts
+  constexpr int kLdsElems = kSplit ? SG::lds_elems(BM) : sched::pipe_lds_elems<D>(BM);
+  static_assert(kLdsElems * 2 <= 160 * 1024, "LDS of one CU");
+  __shared__ __attribute__((aligned(16))) __bf16 lds[kLdsElems];
+  // K and V of LDS tile t; K and V^T rows of step j (keys 64j.., or for key group g
+  // keys 128j + 64g..)
+  auto k_tile = [&](int t) { return kSplit ? lds + SG::k_slot_elem(t) : lds + (t % TL::kStages) * TL::kStageElems; };
+  auto v_tile = [&](int t) {
+    return kSplit ? lds + SG::v_slot_elem(t) : lds + (t % TL::kStages) * TL::kStageElems + KE;
+  };
 
   const Tile tile = decode_tile(a.table, a.H, BM, a.causal, blockIdx.x);
   if (!tile.valid) return;
@@ -143,13 +164,15 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   const int n = lane & 31;
   const int hf = lane >> 5;
   const float c = a.c;
-  const int qr = q0 + wave * 32 + n;  // this lane's query (relative to the segment)
-  const int qmin = q0 + wave * 32;    // the wave's first query
+  const int grp = kSplit ? wave / QB : 0;  // key group (wave-uniform)
+  const int qb = kSplit ? wave % QB : wave;  // 32-query block
+  const int qr = q0 + qb * 32 + n;  // this lane's query (relative to the segment)
+  const int qmin = q0 + qb * 32;    // the wave's first query
 
   // keys this q-tile needs: all of the segment, or (causal) up to its last query
   const int kend = a.causal ? min(L, q0 + BM) : L;
   const int ntiles = (kend + BN - 1) / BN;
-  const int nsteps = (kend + SK - 1) / SK;
+  const int nsteps = kSplit ? ntiles : (kend + SK - 1) / SK;  // steps of this wave
 
   // ---- LDS DMA plan (as in attn_fwd_bf16): DMA instruction i of a tile fills 64
   // consecutive 16-byte slots; wave w issues instructions w, w+8, ...  K slot s is row
@@ -171,8 +194,8 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     const int last = L - 1 - kt0;
     const __bf16* kb = kg + static_cast<size_t>(kt0) * ldk;
     const __bf16* vb = vg + static_cast<size_t>(kt0) * ldv;
-    __bf16* kl = lds + (t % TL::kStages) * TL::kStageElems;
-    __bf16* vl = kl + TL::kKElems;
+    __bf16* kl = k_tile(t);
+    __bf16* vl = v_tile(t);
     if (last >= BN - 1) {
 #pragma unroll
       for (int u = 0; u < KDMA_W; ++u) {
@@ -206,33 +229,43 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   const int my_kdma = KDMA / W + (wave < KDMA % W ? 1 : 0);
   const int my_vdma = VDMA / W + (wave < VDMA % W ? 1 : 0);
 
-  // ---- prologue: Q tile (to the third stage), tiles 0 and 1.  Q rows and K of tile
+  // ---- prologue: Q tile (from the third stage on), tiles 0 and 1.  Q rows and K of tile
   // 0 are waited for before the first barrier; V of tile 0 and tile 1 at the barrier
-  // of iteration 1.
-  constexpr int QDMA = BM * D / 8 / 64;
-  constexpr int QDMA_W = QDMA / W;
-  static_assert(QDMA % W == 0 && BM * D <= TL::kStageElems, "Q tile must fit one stage");
+  // of iteration 1.  Key-split: Q after the K and V rings; K of tiles 0 and 1, then V
+  // of tile 0; K of tile 1 is waited for at the barrier of iteration 0.
+  // Q slot s (16 bytes) is row s/KSL, piece min(s%KSL, D/8-1), as for K
+  constexpr int QDMA = TL::q_pad_dma(BM);
+  constexpr int QDMA_W = (QDMA + W - 1) / W;
   static_assert(W == 4 || W == 8, "4 or 8 waves");
-  __bf16* ql = lds + (TL::kStages - 1) * TL::kStageElems;
+  __bf16* ql = kSplit ? lds + SG::kQElem : lds + sched::pipe_q_elem<D>();
+  static_assert((kSplit ? SG::kQElem : sched::pipe_q_elem<D>()) + QDMA * 512 <= kLdsElems, "Q DMA inside LDS");
 #pragma unroll
   for (int u = 0; u < QDMA_W; ++u) {
     const int i = wave + W * u;
     const int slot = i * 64 + lane;
-    const int row = min(q0 + slot / (D / 8), L - 1);
-    dma16(qg + static_cast<size_t>(row) * a.ldq + (slot % (D / 8)) * 8,
-          __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
+    const int row = min(q0 + slot / KSL, L - 1);
+    if (QDMA % W == 0 || i < QDMA)
+      dma16(qg + static_cast<size_t>(row) * a.ldq + min(slot % KSL, D / 8 - 1) * 8,
+            __builtin_amdgcn_readfirstlane(lds_addr(ql + i * 512)));
   }
-  issue_tile(0, 1);
-  issue_tile(0, 2);
-  static_assert(sched::kPipePrologueTiles == 2, "tiles 0 and 1 before the first barrier");
-  if (ntiles > 1) issue_tile(1, kRope ? 1 : 3);  // with kRope, V of tile 1 after the angle table
+  if constexpr (kSplit) {
+    issue_tile(0, 1);
+    if (ntiles > 1) issue_tile(1, 1);
+    issue_tile(0, 2);
+  } else {
+    issue_tile(0, 1);
+    issue_tile(0, 2);
+    static_assert(sched::kPipePrologueTiles == 2, "tiles 0 and 1 before the first barrier");
+    if (ntiles > 1) issue_tile(1, kRope ? 1 : 3);  // with kRope, V of tile 1 after the angle table
+  }
   // RoPE angles of this lane's query: fragment st holds channels 16st + 8hf + [0, 8),
   // i.e. 4 pairs of one half of the head (the width half below D/2, rotated by the
   // column + 1; the height half by the row + 1), pair index (channel mod D/2) / 2.
   // The workgroup's queries span few patch rows and columns (a 256-token piece of a
   // 32x32 window: 8 rows, 32 columns), so the angles are computed once per (row or
-  // column, frequency) into a table in stage 1's V region -- free until V of tile 1 is
-  // issued, after it -- and each lane reads its 24; a workgroup spanning more positions than the
+  // column, frequency) into a table in stage 1's V region (key-split: V slot 2) -- free
+  // until V of tile 1 (2) is issued, after the first barrier -- and each lane reads its
+  // 24; a workgroup spanning more positions than the
   // table holds computes its lanes' angles directly.  Either way each angle is
   // rope_angle(pos, inv_freq[i]), as in the RoPE pass.
   float rc[KS][4], rs[KS][4];
@@ -240,7 +273,7 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     constexpr int NF = D / 4;                            // frequencies per half
     constexpr int kTabOff = 4 * W;                       // ints of the bounding boxes
     constexpr int kCap = (TL::kVElems * 2 - kTabOff * 4) / (NF * 8);  // positions the table holds
-    int* box = reinterpret_cast<int*>(lds + TL::kStageElems + TL::kKElems);  // V region of stage 1
+    int* box = reinterpret_cast<int*>(v_tile(kSplit ? 2 : 1));
     float* tab = reinterpret_cast<float*>(box + kTabOff);
     int prow = 0, pcol = 0;
     token_patch(a.rope.tb, a.rope.win, static_cast<int>(t0) + min(qr, L - 1), &prow, &pcol);
@@ -295,13 +328,14 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
         }
     }
   }
-  dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + (kRope ? 0 : my_vdma) : 0));
+  if constexpr (kSplit) dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma : 0));
+  else dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + (kRope ? 0 : my_vdma) : 0));
   __syncthreads();
-  if (kRope && ntiles > 1) issue_tile(1, 2);  // the angle table in stage 1's V region is dead now
+  if (!kSplit && kRope && ntiles > 1) issue_tile(1, 2);  // the angle table in stage 1's V region is dead now
 
   bf16x8 qf[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(ql + (wave * 32 + n) * D + 16 * s + 8 * hf);
+  for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(ql + (qb * 32 + n) * KP + 16 * s + 8 * hf);
   if constexpr (kRope) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
@@ -332,7 +366,22 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   f32x16 s[NB];       // S(j) until the softmax has read it, then S(j+1)
   bf16x8 p[NB][2];    // P(j-1) until PV(j-1) has read it, then P(j)
 
-  auto stage_of = [&](int step) { return lds + ((step / NSTEP) % TL::kStages) * TL::kStageElems; };
+  // K and V^T rows of this wave's step j.  Key-split: the ring offset goes through
+  // readfirstlane, an opaque wave-uniform value, so the compiler forms each operand
+  // read as one base plus an immediate instead of re-deriving the ring index per read.
+  auto k_step = [&](int j) {
+    if constexpr (kSplit)
+      return lds + __builtin_amdgcn_readfirstlane(SG::k_slot_elem(j) + grp * SK * KP);
+    else
+      return k_tile(j / NSTEP) + (j % NSTEP) * SK * KP;
+  };
+  auto v_step = [&](int j) {
+    if constexpr (kSplit)
+      return lds + __builtin_amdgcn_readfirstlane(SG::v_slot_elem(j) + grp * SK * VP);
+    else
+      return v_tile(j / NSTEP) + (j % NSTEP) * SK * VP;
+  };
+  static_assert(NB * 32 == SK, "a step is NB blocks of 32 keys");
   // V^T transpose-read lane addressing (see attn_bf16.hpp)
   const int tr_row = ((lane & 15) >> 2) + 4 * hf;
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -350,7 +399,7 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
 
   // Scores of step j past the segment end or (causal) after the query: -inf.
   auto mask = [&](int j) {
-    const int key0 = j * SK;
+    const int key0 = kSplit ? j * BN + grp * SK : j * SK;
     if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -375,8 +424,8 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     }
     if constexpr (SM) mask(j);
     const int jv = sched::pipe_v_step(j), jk = sched::pipe_k_step(j);
-    const __bf16* vt = PV ? stage_of(jv) + TL::kKElems + (jv % NSTEP) * NB * 32 * VP : lds;
-    const __bf16* ks = QK ? stage_of(jk) + (jk % NSTEP) * NB * 32 * KP : lds;
+    const __bf16* vt = PV ? v_step(jv) : lds;
+    const __bf16* ks = QK ? k_step(jk) : lds;
     bf16x8 vf[NPV];
     bf16x8 kf[NQK];
     if constexpr (PV) {
@@ -466,21 +515,33 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     if constexpr (!SM) resc = 0;
   };
 
-  auto tile_sync = [&](int j) {  // start of odd iteration j = 2t+1
-    if (!sched::pipe_syncs(j)) return;
-    dma_wait();  // this wave's DMA of tile t+1
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const int tn = sched::pipe_issue_tile(j);
-    if (tn < ntiles) issue_tile(tn, 3);
+  auto tile_sync = [&](int j) {  // start of iteration j
+    if constexpr (kSplit) {
+      // all of this wave's DMA but V of tile j (the last it issued, read in iteration
+      // j+1), so K of tile j+1 and V of tile j-1 are here; after the barrier the slots
+      // of K of tile j and V of tile j-2 (last read in iteration j-1) are free
+      dma_wait_leave(j < ntiles ? my_vdma : 0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (sched::split_issue_k(j) < ntiles) issue_tile(sched::split_issue_k(j), 1);
+      if (sched::split_issue_v(j) < ntiles) issue_tile(sched::split_issue_v(j), 2);
+    } else {  // odd iterations j = 2t+1
+      if (!sched::pipe_syncs(j)) return;
+      dma_wait();  // this wave's DMA of tile t+1
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int tn = sched::pipe_issue_tile(j);
+      if (tn < ntiles) issue_tile(tn, 3);
+    }
   };
 
   using T_ = std::true_type;
   using F_ = std::false_type;
   // ---- S(0), then iteration 0 (no PV)
   {
-    const __bf16* ks = stage_of(0);
+    const __bf16* ks = k_step(0);
     static_for<NQK>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       const bf16x8 kf = read_k(ks, i);
@@ -490,6 +551,7 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
         s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[PT::qk_s(i)], s[PT::qk_b(i)], 0, 0, 0);
     });
   }
+  tile_sync(0);
   if (nsteps > 1) iteration(0, F_{}, T_{}, T_{}, T_{});
   else iteration(0, F_{}, F_{}, T_{}, T_{});
   // ---- steady state: every part present
@@ -512,11 +574,43 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   // ---- epilogue (as attn_fwd_bf16): O / l -> bf16 (RNE), staged through the wave's
   // own LDS rows once every wave is done with the K/V stages, stored as whole rows
   // (non-temporal), rows inside the segment only.
-  const float inv = 1.0f / half_swap_sum(l_run);
   constexpr int OP = D + 8;
-  static_assert(W * 32 * OP <= TL::kStages * TL::kStageElems, "O staging must fit in the K/V stages");
+  static_assert(QB * 32 * OP <= kLdsElems, "O staging must fit in the K/V stages");
   __syncthreads();
-  __bf16* ow = lds + wave * 32 * OP;
+  if constexpr (kSplit) {
+    // group 1 hands each lane's (O, m, l) -- 13 float4, lane-major, after group 0's
+    // staging rows -- to the group-0 wave of the same queries, which merges:
+    // m = max(m0, m1), O = O0 2^((m0-m)c) + O1 2^((m1-m)c), l likewise
+    constexpr int kPart = CT * 4 + 1;
+    static_assert(QB * 32 * OP * 2 % 16 == 0 && QB * 32 * OP * 2 + QB * kPart * 64 * 16 <= kLdsElems * 2,
+                  "merge buffer must fit behind the staging rows");
+    f32x4* part = reinterpret_cast<f32x4*>(lds + QB * 32 * OP) + qb * kPart * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          part[(ct * 4 + r4) * 64] = f32x4{o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
+      part[CT * 4 * 64] = f32x4{m_run, l_run, 0.0f, 0.0f};
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const f32x4 ml = part[CT * 4 * 64];
+    const float m_new = fmaxf(m_run, ml[0]);
+    const float f0 = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+    const float f1 = __builtin_amdgcn_exp2f((ml[0] - m_new) * c);
+    l_run = __builtin_fmaf(l_run, f0, ml[1] * f1);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 v1 = part[(ct * 4 + r4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[ct][4 * r4 + e] = __builtin_fmaf(o[ct][4 * r4 + e], f0, v1[e] * f1);
+      }
+  }
+  const float inv = 1.0f / half_swap_sum(l_run);
+  __bf16* ow = lds + qb * 32 * OP;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll

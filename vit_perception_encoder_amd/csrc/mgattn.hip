@@ -40,25 +40,42 @@ int block_m_of(int d, int dtype) {
   return dtype == MGATTN_BF16 ? Bf16Tile<96>::kBlockM : F32Tile<96>::kBlockM;
 }
 
-// Query-tile height of one dense call.  The bf16 head_dim-96 kernel runs 8 or 4 waves
-// of 32 queries per workgroup: 256 queries when the (segment, head, tile) units give at
-// least one workgroup per CU, else 128 (a single 1024-token segment of 16 heads is 64
-// units of 256 but 128 of 128, one wave per SIMD on twice the CUs: 25 -> 19 us).
-// Two waves per workgroup (64 queries) ran an order of magnitude slower and are not
-// used.  Other kernels have one tile height.
+// Workgroup shape of one dense call of the bf16 head_dim-96 kernel, which runs 8 or 4
+// waves of 32 queries: 256 queries (8 waves) when the (segment, head, tile) units give
+// at least one workgroup per CU.  With fewer, a non-causal call splits every tile's
+// keys between two wave groups (attn_fwd_bf16_pipe<.., true>): 128-query tiles of 8
+// waves when those fill the CUs, else 64-query tiles of 4 waves (a single 1024-token
+// segment of 16 heads: 64 units of 256, 256 units of 64, each wave taking 8 of the 16
+// key steps).  A causal call keeps whole keys per wave: 128-query tiles of 4 waves.
+// Other kernels have one tile height.
 constexpr int kFillWorkgroups = 256;  // CUs of an MI355X
-int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype) {
-  if (dtype != MGATTN_BF16 || d != 96) return block_m_of(d, dtype);
+enum class DenseKind { kFull8, kFull4, kSplit8, kSplit4, kOther };
+int64_t dense_units(const int32_t* cu, int n_seg, int H, int bm) {
   int64_t units = 0;
-  for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + 255) / 256;
-  return units * H >= kFillWorkgroups ? 256 : 128;
+  for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + bm - 1) / bm;
+  return units * H;
+}
+DenseKind dense_kind(const int32_t* cu, int n_seg, int H, int d, int dtype, int causal) {
+  if (dtype != MGATTN_BF16 || d != 96) return DenseKind::kOther;
+  if (dense_units(cu, n_seg, H, 256) >= kFillWorkgroups) return DenseKind::kFull8;
+  if (causal) return DenseKind::kFull4;
+  return dense_units(cu, n_seg, H, 128) >= kFillWorkgroups ? DenseKind::kSplit8 : DenseKind::kSplit4;
+}
+int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype, int causal) {
+  switch (dense_kind(cu, n_seg, H, d, dtype, causal)) {
+    case DenseKind::kFull8: return 256;
+    case DenseKind::kFull4: return 128;
+    case DenseKind::kSplit8: return 128;
+    case DenseKind::kSplit4: return 64;
+    default: return block_m_of(d, dtype);
+  }
 }
 
 long lds_bytes_of(int d, int dtype) {
   if (dtype == MGATTN_BF16) {
     switch (d) {
       case 64: return Bf16Tile<64>::kLdsBytes;
-      case 96: return Bf16Tile<96>::kLdsBytes;
+      case 96: return sched::pipe_lds_elems<96>(256) * 2;  // the pipelined kernel, 256-query tiles
       case 128: return Bf16Tile<128>::kLdsBytes;
     }
   } else {
@@ -238,7 +255,8 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
   const bool general = cuk != nullptr || Hkv != H || window != 0;
   const bool pack = general && dtype == MGATTN_BF16;
   const int H_tiles = pack ? Hkv : H;
-  const int bm = general ? block_m_of(d, dtype) : dense_block_m(cu, n_seg, H, d, dtype);
+  const DenseKind kind = general ? DenseKind::kOther : dense_kind(cu, n_seg, H, d, dtype, causal);
+  const int bm = general ? block_m_of(d, dtype) : dense_block_m(cu, n_seg, H, d, dtype, causal);
   std::vector<Launch> plan;
   if (!make_plan(cu, cuk, n_seg, H_tiles, bm, plan, pack ? H / Hkv : 1)) return MGATTN_ERR_SIZE;
   if (!device_ok()) return MGATTN_ERR_DEVICE;
@@ -298,12 +316,21 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
                        : launch_all(attn_fwd_bf16<64, false>, Bf16Tile<64>::kThreads, plan, args, s);
       case 96:
         if (general) return launch_all(attn_fwd_bf16<96, true>, Bf16Tile<96>::kThreads, plan, args, s);
-        if (rope) {
-          if (bm == 128) return launch_all(attn_fwd_bf16_pipe<96, 4, true>, 4 * 64, plan, args, s);
-          return launch_all(attn_fwd_bf16_pipe<96, 8, true>, 8 * 64, plan, args, s);
+        switch (kind) {
+          case DenseKind::kFull8:
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true>, 8 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 8>, 8 * 64, plan, args, s);
+          case DenseKind::kFull4:
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 4, true>, 4 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 4>, 4 * 64, plan, args, s);
+          case DenseKind::kSplit8:
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true, true>, 8 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 8, false, true>, 8 * 64, plan, args, s);
+          case DenseKind::kSplit4:
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 4, true, true>, 4 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 4, false, true>, 4 * 64, plan, args, s);
+          default: return MGATTN_ERR_HEAD_DIM;
         }
-        if (bm == 128) return launch_all(attn_fwd_bf16_pipe<96, 4>, 4 * 64, plan, args, s);
-        return launch_all(attn_fwd_bf16_pipe<96, 8>, 8 * 64, plan, args, s);
       case 128:
         return general ? launch_all(attn_fwd_bf16<128, true>, Bf16Tile<128>::kThreads, plan, args, s)
                        : launch_all(attn_fwd_bf16<128, false>, Bf16Tile<128>::kThreads, plan, args, s);
@@ -488,7 +515,7 @@ int mgattn_dense_block_m(int d, int dtype) {
 int mgattn_dense_plan_block_m(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal) {
   const int nl = mgattn_dense_plan(cu_seqlens, n_seg, H, d, dtype, causal, nullptr, 0);
   if (nl < 0) return nl;
-  return dense_block_m(cu_seqlens, n_seg, H, d, dtype);
+  return dense_block_m(cu_seqlens, n_seg, H, d, dtype, causal);
 }
 
 int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal,
@@ -504,7 +531,7 @@ int mgattn_dense_plan(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
     if (cu_seqlens[g + 1] < cu_seqlens[g]) return MGATTN_ERR_SEQLENS;
   if (cu_seqlens[n_seg] <= 0) return MGATTN_ERR_SEQLENS;
   std::vector<Launch> plan;
-  if (!make_plan(cu_seqlens, nullptr, n_seg, H, dense_block_m(cu_seqlens, n_seg, H, d, dtype), plan))
+  if (!make_plan(cu_seqlens, nullptr, n_seg, H, dense_block_m(cu_seqlens, n_seg, H, d, dtype, causal), plan))
     return MGATTN_ERR_SIZE;
   for (int i = 0; i < static_cast<int>(plan.size()) && i < max_launches; ++i)
     if (grids) grids[i] = plan[i].grid;
@@ -517,7 +544,7 @@ int mgattn_dense_tile(const int32_t* cu_seqlens, int n_seg, int H, int d, int dt
   const int nl = mgattn_dense_plan(cu_seqlens, n_seg, H, d, dtype, causal, nullptr, 0);
   if (nl < 0) return nl;
   std::vector<Launch> plan;
-  const int bm = dense_block_m(cu_seqlens, n_seg, H, d, dtype);
+  const int bm = dense_block_m(cu_seqlens, n_seg, H, d, dtype, causal);
   make_plan(cu_seqlens, nullptr, n_seg, H, bm, plan);
   if (launch < 0 || launch >= nl || block < 0 || block >= plan[launch].grid) return MGATTN_ERR_SIZE;
   const Tile t = decode_tile(plan[launch].table, H, bm, causal, static_cast<int>(block));

@@ -40,6 +40,13 @@ struct Geometry {
   static constexpr MGATTN_HD int v_dma_of(int w, int W) { return kVDma / W + (w < kVDma % W ? 1 : 0); }
   // Q tile of bm rows, 16 bytes per lane
   static constexpr MGATTN_HD int q_dma(int bm) { return bm * D / 8 / 64; }
+  // the same with rows padded like K rows (kKSlots slots of 16 bytes, the last one
+  // repeating the row's last piece), as the pipelined kernel stores Q
+  static constexpr MGATTN_HD int q_pad_dma(int bm) { return (bm * kKSlots + 63) / 64; }
+  static constexpr MGATTN_HD int q_pad_dma_of(int w, int W, int bm) {
+    return q_pad_dma(bm) / W + (w < q_pad_dma(bm) % W ? 1 : 0);
+  }
+  static constexpr MGATTN_HD int q_pad_elems(int bm) { return bm * kKPitch; }
 };
 
 // ---- the phased kernel (attn_fwd_bf16): two wave groups one phase apart, a barrier
@@ -60,15 +67,45 @@ constexpr MGATTN_HD int phased_wait_phase(int t, int steps_per_tile) { return 2 
 
 // ---- the pipelined kernel (attn_fwd_bf16_pipe): iteration j runs PV of step j-1, QK
 // of step j+1 and the softmax of step j; QK of step 0 runs before iteration 0.  Tile t
-// sits in stage t % 3 (the Q tile in stage 2 until tile 2 arrives).  Tiles 0 and 1
-// are issued before the first barrier, which publishes Q and K of tile 0; odd
-// iterations open with a wait for all of the wave's DMA, a barrier, and the issue of
-// tile pipe_issue_tile(j).
+// sits in stage t % 3; the Q tile (rows padded like K rows) starts at stage 2 and, for
+// 256 rows, runs past its end, until tile 2 arrives.  Tiles 0 and 1 are issued before
+// the first barrier, which publishes Q and K of tile 0; odd iterations open with a
+// wait for all of the wave's DMA, a barrier, and the issue of tile pipe_issue_tile(j).
 constexpr MGATTN_HD int pipe_k_step(int j) { return j + 1; }       // K read by iteration j (QK)
 constexpr MGATTN_HD int pipe_v_step(int j) { return j - 1; }       // V read by iteration j (PV)
 constexpr MGATTN_HD bool pipe_syncs(int j) { return (j & 1) != 0; }
 constexpr MGATTN_HD int pipe_issue_tile(int j) { return (j >> 1) + 2; }
 constexpr int kPipePrologueTiles = 2;
+template <int D>
+constexpr MGATTN_HD int pipe_q_elem() { return (Geometry<D>::kStages - 1) * Geometry<D>::kStageElems; }
+template <int D>
+constexpr MGATTN_HD int pipe_lds_elems(int bm) {
+  return imax(Geometry<D>::kStages * Geometry<D>::kStageElems, pipe_q_elem<D>() + Geometry<D>::q_pad_elems(bm));
+}
+
+// ---- the key-split pipelined kernel (attn_fwd_bf16_pipe<D, W, R, true>), for launches
+// with too few (segment, head, query tile) units to fill the chip: two wave groups
+// share every 128-key tile, group g taking keys 64g .. 64g+63 of it, so a wave's step
+// j is half of tile j and each iteration consumes a whole tile.  Iteration j reads K
+// of tile j+1 (QK) and V of tile j-1 (PV); K tiles live in a ring of two slots, V
+// tiles in a ring of three, the Q tile after them.  Before QK(0): DMA of Q, K of tiles
+// 0 and 1 and V of tile 0, a wait for Q and K of tile 0, a barrier.  Every iteration j
+// (the closing PV-only one included) opens with a wait for all of the wave's DMA but
+// V of tile j (the last it issued), a barrier, and the DMA of K of tile j+2 and V of
+// tile j+1 (those that exist), in that order.
+template <int D>
+struct SplitGeometry : Geometry<D> {
+  using G = Geometry<D>;
+  static constexpr int kKRing = 2, kVRing = 3;
+  static constexpr MGATTN_HD int k_slot_elem(int t) { return (t % kKRing) * G::kKElems; }
+  static constexpr MGATTN_HD int v_slot_elem(int t) { return kKRing * G::kKElems + (t % kVRing) * G::kVElems; }
+  static constexpr int kQElem = kKRing * G::kKElems + kVRing * G::kVElems;
+  static constexpr MGATTN_HD int lds_elems(int bm) { return kQElem + G::q_pad_elems(bm); }
+};
+constexpr MGATTN_HD int split_issue_k(int j) { return j + 2; }  // K tile issued after iteration j's barrier
+constexpr MGATTN_HD int split_issue_v(int j) { return j + 1; }  // V tile issued after it
+constexpr MGATTN_HD int split_k_tile(int j) { return j + 1; }   // K tile read by iteration j
+constexpr MGATTN_HD int split_v_tile(int j) { return j - 1; }   // V tile read by iteration j
 
 }  // namespace sched
 }  // namespace mgattn
