@@ -19,10 +19,16 @@ segment), ms per step (= ms per tower), the roofline of the attention kernel, an
 the f64 CPU oracle timed on a bounded sample of the same workload on this host.
 
     python bench.py [--steps K] [--warmup W] [--eager] [--no-cpu-baseline] [--copy-calibration]
+
+Counter summaries from rocprofv3 --pmc runs of this script (no GPU needed):
+
+    python bench.py --write-traffic FETCH_CSV WRITE_CSV   # HBM bytes per launch -> profiles/
+    python bench.py --counter-table CSV [CSV ...]         # mean per dispatch, full / window layers
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -72,6 +78,96 @@ def traffic_per_launch():
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+TOWER_GRID = 256 * 512  # threads of one tower launch: 256 workgroups of 8 waves
+COPY_KERNEL = "__amd_rocclr_copyBuffer"  # the runtime's device-to-device copy (--copy-calibration)
+COPY_BYTES = 1 << 30
+
+
+def _dispatches(path):
+    """rocprofv3 counter_collection CSV -> [(dispatch id, kernel name, grid size,
+    {counter: value summed over the counter's instances})] in dispatch order."""
+    d = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            ent = d.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]), {}])
+            ent[2][r["Counter_Name"]] = ent[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [(k, v[0], v[1], v[2]) for k, v in sorted(d.items())]
+
+
+def _is_tower_kernel(name: str, grid: int) -> bool:
+    return KERNEL_NAME in name and grid == TOWER_GRID
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> int:
+    """HBM bytes per launch of the tower's attention kernel from one FETCH_SIZE run and
+    one WRITE_SIZE run of `bench.py --eager --copy-calibration` under rocprofv3 --pmc:
+    median KiB per dispatch over the tower-shaped launches (full and window layers
+    move the same Q, K, V and O), each counter scaled so that the run's 1 GiB device
+    copy reads as 1 GiB.  Writes TRAFFIC_FILE, stamped with the current kernel sources'
+    hash (the CSVs must come from a build of these sources)."""
+    out = {"what": f"HBM traffic of {KERNEL_NAME} per launch on the 50-layer tower schedule at 4096 tokens "
+                   "(full and window launches alike move Q, K, V and O of 4096 x 1536 bf16); median over the "
+                   "run's tower-shaped launches",
+           "kernel_source_sha256": kernel_source_hash(),
+           "command_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o p -- python3 -u bench.py "
+                            "--steps 2 --warmup 1 --no-cpu-baseline --eager --copy-calibration",
+           "command_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR -o p -- python3 -u bench.py "
+                            "--steps 2 --warmup 1 --no-cpu-baseline --eager --copy-calibration",
+           "command_summary": f"python bench.py --write-traffic {fetch_csv} {write_csv}"}
+    per = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _dispatches(path)
+        att = [c[counter] for _, n, g, c in rows if _is_tower_kernel(n, g) and counter in c]
+        cpy = sorted(c[counter] for _, n, _, c in rows if n == COPY_KERNEL and counter in c)[-3:]
+        if not att or not cpy:
+            print(f"[bench] {path}: no tower launches or no calibration copy", file=sys.stderr)
+            return 1
+        kib = float(np.median(att))
+        scale = round(COPY_BYTES / (float(np.median(cpy)) * 1024.0), 3)
+        per[counter] = (kib, scale, len(att))
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        out[f"{key}_kib_per_dispatch_raw"] = kib
+        out.setdefault("calibration", {"copy_bytes": COPY_BYTES})[f"{key}_kib_raw"] = float(np.median(cpy))
+        out["calibration"][f"{key}_scale"] = scale
+    out["attention_dispatches"] = per["FETCH_SIZE"][2]
+    fb = int(round(per["FETCH_SIZE"][0] * 1024 * per["FETCH_SIZE"][1]))
+    wb = int(round(per["WRITE_SIZE"][0] * 1024 * per["WRITE_SIZE"][1]))
+    alg = 4 * 4096 * 16 * 96 * 2
+    out.update({"hbm_fetch_bytes_per_launch": fb, "hbm_write_bytes_per_launch": wb, "hbm_bytes_per_launch": fb + wb,
+                "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 3)})
+    TRAFFIC_FILE.write_text(json.dumps(out, indent=1) + "\n")
+    print(json.dumps(out, indent=1))
+    return 0
+
+
+def counter_table(paths) -> int:
+    """Markdown table of counters per dispatch (summed over instances, mean over
+    dispatches) of the tower's attention launches in runs of `bench.py --eager
+    --no-token-path`, split into full and window layers: the i-th tower launch of a
+    run is layer i mod 50 of the schedule."""
+    from vit_perception_encoder_amd import workloads as wl
+    kinds = wl.tower_layer_kinds()
+    acc = {"full": {}, "window": {}}
+    cnt = {"full": {}, "window": {}}
+    for path in paths:
+        i = 0
+        for _, n, g, c in _dispatches(path):
+            if not _is_tower_kernel(n, g):
+                continue
+            kind = kinds[i % len(kinds)]
+            i += 1
+            for name, v in c.items():
+                acc[kind][name] = acc[kind].get(name, 0.0) + v
+                cnt[kind][name] = cnt[kind].get(name, 0) + 1
+    names = sorted(set(acc["full"]) | set(acc["window"]))
+    print("| counter | full | window |\n|---|---|---|")
+    for name in names:
+        f = acc["full"].get(name, 0.0) / max(cnt["full"].get(name, 0), 1)
+        w = acc["window"].get(name, 0.0) / max(cnt["window"].get(name, 0), 1)
+        print(f"| {name} | {f:.4g} | {w:.4g} |")
+    return 0
 
 
 def host_threads() -> int:
@@ -469,6 +565,10 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="launch the 50 layers eagerly instead of replaying a graph")
     ap.add_argument("--no-token-path", action="store_true",
                     help="skip detail.token_path (profiling runs that count only the tower's launches)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 --pmc counter_collection CSVs and exit")
+    ap.add_argument("--counter-table", nargs="+", metavar="CSV",
+                    help="print mean counters per tower launch (full / window) from rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     ap.add_argument("--shape-sweep", action="store_true",
@@ -478,8 +578,12 @@ def main() -> int:
                     help="print the attention kernel's time at 4096 tokens for segment lengths 256..4096 "
                          "(fixed cost per launch vs cost per 64-key step) and exit; no JSON line")
     args = ap.parse_args()
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
+    if args.counter_table:
+        return counter_table(args.counter_table)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: mgattn has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
 
     import torch

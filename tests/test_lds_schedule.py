@@ -43,8 +43,6 @@ def test_kernel_schedules_are_race_free(model):
     "pipe_prologue_short",         # the prologue waits for one DMA too few
     "phased_issue_early",          # a stage refilled two phases early
     "phased_wait_late",            # a tile waited for two phases late
-    "rope_table_no_barrier",       # the RoPE angle table read before every wave stored it
-    "rope_tile1_early",            # tile 1's DMA over the angle table other waves still read
     "split_k_early",               # key-split: K of tile j+3 into the slot of K of tile j+1
     "split_leave_k",               # key-split: K of tile j+1 left in flight at its barrier
     "split_merge_no_barrier",      # key-split: group 0 reads group 1's partials before they are stored

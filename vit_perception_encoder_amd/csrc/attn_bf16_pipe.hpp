@@ -105,9 +105,9 @@ struct PipeTile {
 // W waves per workgroup, 32 queries each: 8 for launches that fill the chip, 4 (query
 // tiles of 128) when a launch has too few (segment, head, tile) units.  kRope: Q is
 // rotated by the 2D RoPE as it is read (mgattn_dense_rope2d); the angles of a lane's 24
-// rotation pairs are computed while the prologue's DMA is in flight, and the rotation
-// rounds exactly as the RoPE pass does (window_rope.hpp), so the result is that of
-// rotating q in memory first.
+// rotation pairs are computed while the prologue's DMA is in flight, and the angles and
+// the rotation round exactly as the RoPE pass does (window_rope.hpp), so the result is
+// that of rotating q in memory first.
 // kSplit: the keys are split between two wave groups of W/2 waves (query tiles of
 // 16W), group g taking the second half of every 128-key tile when g = 1, each wave
 // running its own online softmax over its half; at the end group 1 hands its (m, l, O)
@@ -256,82 +256,31 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     issue_tile(0, 1);
     issue_tile(0, 2);
     static_assert(sched::kPipePrologueTiles == 2, "tiles 0 and 1 before the first barrier");
-    if (ntiles > 1) issue_tile(1, kRope ? 1 : 3);  // with kRope, V of tile 1 after the angle table
+    if (ntiles > 1) issue_tile(1, 3);
   }
-  // RoPE angles of this lane's query: fragment st holds channels 16st + 8hf + [0, 8),
-  // i.e. 4 pairs of one half of the head (the width half below D/2, rotated by the
-  // column + 1; the height half by the row + 1), pair index (channel mod D/2) / 2.
-  // The workgroup's queries span few patch rows and columns (a 256-token piece of a
-  // 32x32 window: 8 rows, 32 columns), so the angles are computed once per (row or
-  // column, frequency) into a table in stage 1's V region (key-split: V slot 2) -- free
-  // until V of tile 1 (2) is issued, after the first barrier -- and each lane reads its
-  // 24; a workgroup spanning more positions than the
-  // table holds computes its lanes' angles directly.  Either way each angle is
-  // rope_angle(pos, inv_freq[i]), as in the RoPE pass.
+  // RoPE angles of this lane's query, computed while the prologue's DMA is in flight:
+  // fragment st holds channels 16st + 8hf + [0, 8), i.e. 4 pairs of one half of the
+  // head (the width half below D/2, rotated by the column + 1; the height half by the
+  // row + 1), pair index (channel mod D/2) / 2; rope_angle_bf16 as in the RoPE pass.
   float rc[KS][4], rs[KS][4];
   if constexpr (kRope) {
-    constexpr int NF = D / 4;                            // frequencies per half
-    constexpr int kTabOff = 4 * W;                       // ints of the bounding boxes
-    constexpr int kCap = (TL::kVElems * 2 - kTabOff * 4) / (NF * 8);  // positions the table holds
-    int* box = reinterpret_cast<int*>(v_tile(kSplit ? 2 : 1));
-    float* tab = reinterpret_cast<float*>(box + kTabOff);
     int prow = 0, pcol = 0;
     token_patch(a.rope.tb, a.rope.win, static_cast<int>(t0) + min(qr, L - 1), &prow, &pcol);
-    int rmin = prow, rmax = prow, cmin = pcol, cmax = pcol;
 #pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      rmin = min(rmin, __shfl_xor(rmin, sh));
-      rmax = max(rmax, __shfl_xor(rmax, sh));
-      cmin = min(cmin, __shfl_xor(cmin, sh));
-      cmax = max(cmax, __shfl_xor(cmax, sh));
-    }
-    if (lane == 0) {
-      box[4 * wave] = rmin;
-      box[4 * wave + 1] = rmax;
-      box[4 * wave + 2] = cmin;
-      box[4 * wave + 3] = cmax;
-    }
-    __syncthreads();
+    for (int st = 0; st < KS; ++st)
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      rmin = min(rmin, box[4 * w]);
-      rmax = max(rmax, box[4 * w + 1]);
-      cmin = min(cmin, box[4 * w + 2]);
-      cmax = max(cmax, box[4 * w + 3]);
-    }
-    const int ncol = cmax - cmin + 1, nrow = rmax - rmin + 1;
-    auto channel = [&](int st, int k) { return 16 * st + 8 * hf + 2 * k; };
-    if (ncol + nrow <= kCap) {  // workgroup-uniform
-      for (int e = tid; e < (ncol + nrow) * NF; e += 64 * W) {
-        const int pi = e / NF, fi = e - pi * NF;
-        const int pos = pi < ncol ? cmin + pi + 1 : rmin + (pi - ncol) + 1;
-        rope_angle(static_cast<float>(pos), a.rope.inv_freq[fi], &tab[2 * e], &tab[2 * e + 1]);
+      for (int k = 0; k < 4; ++k) {
+        const int ch = 16 * st + 8 * hf + 2 * k;
+        rope_angle_bf16(static_cast<float>(ch >= D / 2 ? prow + 1 : pcol + 1), a.rope.inv_freq[(ch % (D / 2)) / 2],
+                        &rc[st][k], &rs[st][k]);
+        // keep the angles here, under the DMA wait: left alone, the compiler sinks them
+        // past the barrier next to the rotation, onto the path to the first MFMA
+        asm volatile("" ::"v"(rc[st][k]), "v"(rs[st][k]));
       }
-      __syncthreads();
-#pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const bool height = channel(st, 0) >= D / 2;
-        const int pi = height ? ncol + prow - rmin : pcol - cmin;
-        const f32x4* src = reinterpret_cast<const f32x4*>(tab + 2 * (pi * NF + (channel(st, 0) % (D / 2)) / 2));
-        const f32x4 lo = src[0], hi = src[1];  // (c, s) of the fragment's 4 pairs
-        rc[st][0] = lo[0]; rs[st][0] = lo[1]; rc[st][1] = lo[2]; rs[st][1] = lo[3];
-        rc[st][2] = hi[0]; rs[st][2] = hi[1]; rc[st][3] = hi[2]; rs[st][3] = hi[3];
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < KS; ++st)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int ch = channel(st, k);
-          rope_angle(static_cast<float>(ch >= D / 2 ? prow + 1 : pcol + 1), a.rope.inv_freq[(ch % (D / 2)) / 2],
-                     &rc[st][k], &rs[st][k]);
-        }
-    }
   }
   if constexpr (kSplit) dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma : 0));
-  else dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + (kRope ? 0 : my_vdma) : 0));
+  else dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + my_vdma : 0));
   __syncthreads();
-  if (!kSplit && kRope && ntiles > 1) issue_tile(1, 2);  // the angle table in stage 1's V region is dead now
 
   bf16x8 qf[KS];
 #pragma unroll

@@ -45,20 +45,23 @@ __device__ inline int image_of(const ImageTable& tb, int t) {
 // Raster index (y*gw + x) of the token at position p of an image's window order.
 // Every block row but the last is win rows tall and spans win*gw tokens; inside a
 // block row of height bh, every block but the last is win columns wide and spans
-// bh*win tokens.
+// bh*win tokens.  The block size is clamped to each side of the image (win may exceed
+// the grid: one block per image); blocks are clipped at the edges anyway, so the
+// order is the same, and every product below is then at most gh*gw < 2^31, which
+// keeps the divisions in 32 bits.
 __device__ inline int window_to_raster(int p, int gh, int gw, int win) {
-  // 64-bit products: win may exceed the grid (one block per image)
-  const int64_t row_span = static_cast<int64_t>(win) * gw;
-  const int by = static_cast<int>(p / row_span);
-  const int rem = static_cast<int>(p - by * row_span);
-  const int bh = static_cast<int>(min(static_cast<int64_t>(win), static_cast<int64_t>(gh) - static_cast<int64_t>(by) * win));
-  const int64_t blk_span = static_cast<int64_t>(bh) * win;
-  const int bx = static_cast<int>(rem / blk_span);
-  const int rem2 = static_cast<int>(rem - bx * blk_span);
-  const int bw = static_cast<int>(min(static_cast<int64_t>(win), static_cast<int64_t>(gw) - static_cast<int64_t>(bx) * win));
-  const int y = static_cast<int>(static_cast<int64_t>(by) * win + rem2 / bw);
-  const int x = static_cast<int>(static_cast<int64_t>(bx) * win + rem2 % bw);
-  return y * gw + x;
+  const uint32_t wh = static_cast<uint32_t>(min(win, gh)), ww = static_cast<uint32_t>(min(win, gw));
+  const uint32_t ugh = static_cast<uint32_t>(gh), ugw = static_cast<uint32_t>(gw), up = static_cast<uint32_t>(p);
+  const uint32_t row_span = wh * ugw;
+  const uint32_t by = up / row_span;
+  const uint32_t rem = up - by * row_span;
+  const uint32_t bh = min(wh, ugh - by * wh);
+  const uint32_t blk_span = bh * ww;
+  const uint32_t bx = rem / blk_span;
+  const uint32_t rem2 = rem - bx * blk_span;
+  const uint32_t bw = min(ww, ugw - bx * ww);
+  const uint32_t ry = rem2 / bw;
+  return static_cast<int>((by * wh + ry) * ugw + bx * ww + (rem2 - ry * bw));
 }
 
 // Patch coordinates (0-based) of batch token t, for tokens in raster order (win == 0)
@@ -72,20 +75,33 @@ __device__ inline void token_patch(const ImageTable& tb, int win, int t, int* ro
   *col = r % gw;
 }
 
-// Cosine and sine of one rotation pair at 1-based position pos, frequency f.
+// Cosine and sine of one rotation pair at 1-based position pos, frequency f (radians
+// per position), for f32 results.
 __device__ inline void rope_angle(float pos, float f, float* c, float* s) { sincosf(pos * f, s, c); }
+
+// The same for bf16 results, from the hardware sine and cosine (v_sin_f32 / v_cos_f32
+// take the angle in revolutions): the angle pos*f/(2 pi) in f32, reduced to [0, 1) by
+// an exact fraction.  The angle carries a relative error of a few 2^-24 (|angle| <
+// 2^8 revolutions for positions below ~1600 at f <= 1), far below the 2^-8 rounding of
+// the bf16 result.  Every kernel that rotates bf16 (the RoPE pass, the attention
+// kernel rotating Q on load) calls this one, so they agree bit for bit.
+__device__ inline void rope_angle_bf16(float pos, float f, float* c, float* s) {
+  const float rev = __builtin_amdgcn_fractf(pos * f * 0.159154943091895336f);
+  *s = __builtin_amdgcn_sinf(rev);
+  *c = __builtin_amdgcn_cosf(rev);
+}
 
 // One rotation pair stored as two bf16 in a 32-bit word (low half the real part):
 // (re + i im) * (c + i s), rounded to bf16.  The products are written out so that every
 // kernel that rotates (the RoPE pass, the attention kernel rotating Q on load) rounds
 // the same way: fma(re, c, -(im*s)) and fma(re, s, im*c).
 __device__ inline uint32_t rope_pair_bf16(uint32_t w, float c, float s) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const float re = __uint_as_float(w << 16), im = __uint_as_float(w & 0xffff0000u);
   const float ims = im * s, imc = im * c;
-  const __bf16 a2 = static_cast<__bf16>(__builtin_fmaf(re, c, -ims));
-  const __bf16 b2 = static_cast<__bf16>(__builtin_fmaf(re, s, imc));
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a2)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) << 16);
+  // both halves rounded to bf16 (RNE) by one packed conversion
+  const bf16x2_t r = {static_cast<__bf16>(__builtin_fmaf(re, c, -ims)), static_cast<__bf16>(__builtin_fmaf(re, s, imc))};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // dst row p <- src row perm(p) (gather into window order), or dst row perm(p) <- src
@@ -163,8 +179,11 @@ void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
       off[u] = head * a.d + pcs[u] * kPer;
       raw[u] = *reinterpret_cast<const u32x4*>(row + off[u]);
     }
-    if (j0 == 0 && lane < 2 * quarter)  // the angles, while the first loads are in flight
-      rope_angle(static_cast<float>(lane < quarter ? pcol + 1 : prow + 1), f_l, &c_l, &s_l);
+    if (j0 == 0 && lane < 2 * quarter) {  // the angles, while the first loads are in flight
+      const float pos = static_cast<float>(lane < quarter ? pcol + 1 : prow + 1);
+      if constexpr (sizeof(T) == 2) rope_angle_bf16(pos, f_l, &c_l, &s_l);
+      else rope_angle(pos, f_l, &c_l, &s_l);
+    }
     asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]), "v"(raw[3]));
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
