@@ -24,6 +24,7 @@ Counter summaries from rocprofv3 --pmc runs of this script (no GPU needed):
 
     python bench.py --write-traffic FETCH_CSV WRITE_CSV   # HBM bytes per launch -> profiles/
     python bench.py --counter-table CSV [CSV ...]         # mean per dispatch, full / window layers
+    python bench.py --kernel-traffic FETCH_CSV WRITE_CSV  # HBM MB per dispatch of every kernel
 """
 from __future__ import annotations
 
@@ -139,6 +140,33 @@ def write_traffic(fetch_csv: str, write_csv: str) -> int:
                 "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 3)})
     TRAFFIC_FILE.write_text(json.dumps(out, indent=1) + "\n")
     print(json.dumps(out, indent=1))
+    return 0
+
+
+def kernel_traffic(fetch_csv: str, write_csv: str) -> int:
+    """Markdown table of HBM traffic per dispatch for every (kernel, grid size) of one
+    FETCH_SIZE run and one WRITE_SIZE run (medians, each counter scaled by the run's
+    1 GiB calibration copy as in write_traffic)."""
+    med = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _dispatches(path)
+        cpy = sorted(c[counter] for _, n, _, c in rows if n == COPY_KERNEL and counter in c)[-3:]
+        if not cpy:
+            print(f"[bench] {path}: no calibration copy", file=sys.stderr)
+            return 1
+        scale = COPY_BYTES / (float(np.median(cpy)) * 1024.0)
+        groups = {}
+        for _, n, g, c in rows:
+            if counter in c and n != COPY_KERNEL:
+                groups.setdefault((n, g), []).append(c[counter] * 1024.0 * scale)
+        for key, vals in groups.items():
+            med.setdefault(key, {})[counter] = (float(np.median(vals)), len(vals))
+    print("| kernel | grid (threads) | dispatches | fetch (MB) | write (MB) |\n|---|---|---|---|---|")
+    for (n, g), v in sorted(med.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        f, nf = v.get("FETCH_SIZE", (float("nan"), 0))
+        w, _ = v.get("WRITE_SIZE", (float("nan"), 0))
+        short = re.sub(r"\(.*", "", n.replace("void ", "").replace("mgattn::", ""))
+        print(f"| {short} | {g} | {nf} | {f / 1e6:.2f} | {w / 1e6:.2f} |")
     return 0
 
 
@@ -567,6 +595,8 @@ def main() -> int:
                     help="skip detail.token_path (profiling runs that count only the tower's launches)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter_collection CSVs and exit")
+    ap.add_argument("--kernel-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print HBM traffic per dispatch of every kernel from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--counter-table", nargs="+", metavar="CSV",
                     help="print mean counters per tower launch (full / window) from rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -582,6 +612,8 @@ def main() -> int:
         return write_traffic(*args.write_traffic)
     if args.counter_table:
         return counter_table(args.counter_table)
+    if args.kernel_traffic:
+        return kernel_traffic(*args.kernel_traffic)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: mgattn has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
