@@ -218,8 +218,9 @@ int mgattn_dense_supported(int H, int d, int dtype);
 
 /* Bytes of LDS (on-chip shared memory) one workgroup of the (d, dtype) kernel asks
  * for, or a negative mgattn_status if (d, dtype) is not supported.  Pure host
- * arithmetic, no GPU needed; equals the static LDS footprint of the kernel (for bf16
- * head_dim 96, of its largest workgroup shape: the key-split shapes use less). */
+ * arithmetic, no GPU needed; equals the static LDS footprint of the kernel's largest
+ * workgroup shape (bf16 head_dim 96: the 256-query tile; f32: the key-split 32-query
+ * block at head_dim 64 and 96, the 128-query tile at 128). */
 long mgattn_dense_lds_bytes(int d, int dtype);
 
 /* Queries per workgroup of the (d, dtype) kernel (the tallest q-tile it uses), or a
@@ -232,7 +233,9 @@ int mgattn_dense_block_m(int d, int dtype);
  * give at least 256 workgroups (one per CU).  Otherwise a non-causal call splits each
  * tile's keys between two wave groups and takes 128 if the units of 128 give 256
  * workgroups, else 64 (one 1024-token segment of 16 heads: 64 units of 256, 256 of
- * 64); a causal call takes 128.  Every other (d, dtype) has the single height of
+ * 64); a causal call takes 128.  f32 takes 128, or 32 (the keys of each 32-query block
+ * split over the workgroup's waves) for a non-causal call whose 128-query units give
+ * fewer than 256 workgroups.  Every other (d, dtype) has the single height of
  * mgattn_dense_block_m. */
 int mgattn_dense_plan_block_m(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal);
 

@@ -155,6 +155,17 @@ def test_key_split_large_logits(torch):
     _full_check(torch, case)
 
 
+def test_f32_key_split_long_segments(torch):
+    """f32 calls too short to fill the chip run 32-query blocks with the keys split over
+    eight waves (four at head_dim 128): long segments give every wave several 32-key
+    tiles, short ones leave waves without tiles; keys scaled x4 so the waves' maxima
+    differ.  Tolerance 1e-4 (f32)."""
+    for d in (96, 128):
+        case = _rand_case(f"f32_split_d{d}", [2047, 33, 1, 0, 64], H=2, d=d, dtype=wl.F32, seed=18, kscale=4.0)
+        assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, 2, d, wl.F32, 0) == 32
+        _full_check(torch, case)
+
+
 def test_key_split_128_query_tiles(torch):
     """One 2048-token segment of 16 heads: 128 units of 256 queries, 256 of 128, so
     128-query tiles with the keys split between two groups of four waves."""
@@ -324,4 +335,45 @@ def test_graph_capture_replays_match_eager(torch):
         got = from_device(out, torch).reshape(case.T, 2, 96)
         assert np.array_equal(got, want), f"replay {rep} differs from eager"
         # eager work between replays
+        run(torch, other.q, other.k, other.v, other.cu_seqlens, 16, 96, other.scale, 0, wl.BF16)
+
+
+def test_graph_capture_key_split_shapes(torch):
+    """Both key-split shapes captured into one HIP graph (a 1024-token segment of 16
+    heads: 64-query tiles; a 2048-token one: 128-query tiles) replay to the eager
+    results bit for bit, with eager work between the replays."""
+    from tests.gpu_helpers import from_device, to_device
+
+    cases = [_rand_case("graph_split64", [1024], H=16, seed=121), _rand_case("graph_split128", [2048], H=16, seed=122)]
+    for c, bm in zip(cases, (64, 128)):
+        assert mg.mgattn_dense_plan_block_m(c.cu_seqlens, 1, 16, 96, wl.BF16, 0) == bm
+    wants = [run(torch, c.q, c.k, c.v, c.cu_seqlens, 16, 96, c.scale, 0, wl.BF16)[0] for c in cases]
+    dev = [tuple(to_device(x, torch) for x in (c.q, c.k, c.v)) for c in cases]
+    outs = [torch.zeros(c.T, 16 * 96, dtype=torch.bfloat16, device="cuda") for c in cases]
+    cus = [[int(x) for x in c.cu_seqlens] for c in cases]
+
+    def launch(stream):
+        for (q, k, v), o, cu, c in zip(dev, outs, cus, cases):
+            mg.mgattn_dense(q, k, v, o, cu, 1, 16, 96, c.scale, 0, wl.BF16, stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("graph capture, key-split shapes")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch(torch.cuda.current_stream())
+    other = wl.config_window896()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, c, want in zip(outs, cases, wants):
+            got = from_device(o, torch).reshape(c.T, 16, 96)
+            assert np.array_equal(got, want), f"{c.name}: replay {rep} differs from eager"
         run(torch, other.q, other.k, other.v, other.cu_seqlens, 16, 96, other.scale, 0, wl.BF16)

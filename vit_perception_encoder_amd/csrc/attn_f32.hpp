@@ -211,4 +211,176 @@ void attn_fwd_f32(KernelArgs a) {
   }
 }
 
+// Key-split variant for dense non-causal calls whose (segment, head, 128-query tile)
+// units leave most SIMDs idle (a 256-token segment of 16 heads is 32 workgroups of
+// four waves): one 32-query block per workgroup, W waves each taking the 32-key tiles
+// t = wave, wave + W, ... of the segment.  A wave's tiles are its own, so K and V go
+// straight from global memory into the MFMA operand registers (no LDS staging, no
+// barriers in the loop), with the same operand layout as above: lane (n, hf) reads K
+// row n, channels hf*D/2 + [0, D/2), and for PV the V element (key, 32ct + n).  Each
+// wave runs its own online softmax; at the end waves 1..W-1 write (m, l, O) per lane to
+// LDS and wave 0 merges the W states (m = max, weights 2^((m_w - m)c)) and stores.
+// Waves per 32-query block of the key-split f32 kernel (four at head_dim 128, where
+// eight waves would leave too few registers per wave) and its LDS bytes.
+template <int D>
+constexpr int f32_split_waves() { return D == 128 ? 4 : 8; }
+template <int D>
+constexpr long f32_split_lds_bytes() { return (f32_split_waves<D>() - 1) * (D / 32 * 4 + 1) * 64 * 16L; }
+
+template <int D, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W >= 8 ? 2 : 1, 2)))
+void attn_fwd_f32_split(KernelArgs a) {
+  constexpr int BM = 32, BN = 32;
+  constexpr int HD = D / 2;
+  constexpr int CT = D / 32;
+  constexpr int kPart = CT * 4 + 1;  // float4 per lane: O, then (m, l)
+  constexpr float kRescaleLog2 = 8.0f;
+  __shared__ __attribute__((aligned(16))) f32x4 part[(W - 1) * kPart * 64];
+  static_assert(W == f32_split_waves<D>() && sizeof(part) == f32_split_lds_bytes<D>(), "LDS bytes the host reports");
+
+  const Tile tile = decode_tile(a.table, a.H, BM, 0, blockIdx.x);
+  if (!tile.valid) return;
+  const int L = a.table.len[tile.slot];  // queries = keys of the segment
+  const int q0 = tile.q0;
+  const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const float* __restrict__ qg = static_cast<const float*>(a.q) + t0 * a.ldq + hoff;
+  const float* __restrict__ kg = static_cast<const float*>(a.k) + t0 * a.ldk + hoff;
+  const float* __restrict__ vg = static_cast<const float*>(a.v) + t0 * a.ldv + hoff;
+  float* __restrict__ og = static_cast<float*>(a.o) + t0 * a.ldo + hoff;
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const float c = a.c;
+  const int qr = q0 + n;
+
+  float qf[HD];
+  if (qr < L) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(qg + static_cast<size_t>(qr) * a.ldq + hf * HD);
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) {
+      const f32x4 x = p[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * j + e] = x[e] * static_cast<float>(a.qsign);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < HD; ++j) qf[j] = 0.0f;
+  }
+
+  const int ntiles = (L + BN - 1) / BN;
+  f32x16 o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int t = wave; t < ntiles; t += W) {
+    const int kt0 = t * BN;
+    // K row kt0 + n (rows past the segment end read as zeros), channels hf*HD + [0, HD)
+    f32x4 kq[HD / 4];
+    const bool krow = kt0 + n < L;
+    const f32x4* kp = reinterpret_cast<const f32x4*>(kg + static_cast<size_t>(kt0 + n) * a.ldk + hf * HD);
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j) kq[j] = krow ? kp[j] : f32x4{};
+    // V elements (key kt0 + acc_row(r, hf), channel 32ct + n)
+    float vv[16][CT];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt0 + acc_row(r, hf);
+      const float* vr = vg + static_cast<size_t>(key) * a.ldv + n;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) vv[r][ct] = key < L ? vr[ct * 32] : 0.0f;
+    }
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int j = 0; j < HD / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(kq[j][e], qf[4 * j + e], s, 0, 0, 0);
+    const bool masked = kt0 + BN > L;
+    if (masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kt0 + acc_row(r, hf) >= L) s[r] = -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float m_tile = fmaxf(half_swap_max(mx), -1.0e30f);
+    if (t == wave) {
+      m_run = m_tile;
+    } else if (__builtin_amdgcn_ballot_w64((m_tile - m_run) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+    }
+    const float mc = m_run * c;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mc));
+      if (masked && kt0 + acc_row(r, hf) >= L) p = 0.0f;
+      s[r] = p;
+      lsum += p;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][ct], s[r], o[ct], 0, 0, 0);
+  }
+
+  // merge: a wave without tiles holds m = -inf, l = 0, O = 0 and weighs nothing
+  if (wave > 0) {
+    f32x4* pw = part + (wave - 1) * kPart * 64 + lane;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        pw[(ct * 4 + r4) * 64] = f32x4{o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
+    pw[CT * 4 * 64] = f32x4{m_run, l_run, 0.0f, 0.0f};
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  float m_all = m_run;
+#pragma unroll
+  for (int w = 1; w < W; ++w) m_all = fmaxf(m_all, part[(w - 1) * kPart * 64 + CT * 4 * 64 + lane][0]);
+  const float f0 = __builtin_amdgcn_exp2f((m_run - m_all) * c);
+  l_run *= f0;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] *= f0;
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    const f32x4* pw = part + (w - 1) * kPart * 64 + lane;
+    const f32x4 ml = pw[CT * 4 * 64];
+    const float fw = __builtin_amdgcn_exp2f((ml[0] - m_all) * c);
+    l_run = __builtin_fmaf(ml[1], fw, l_run);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 v = pw[(ct * 4 + r4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[ct][4 * r4 + e] = __builtin_fmaf(v[e], fw, o[ct][4 * r4 + e]);
+      }
+  }
+  const float inv = 1.0f / half_swap_sum(l_run);
+  if (qr < L) {
+    float* dst = og + static_cast<size_t>(qr) * a.ldo + 4 * hf;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = o[ct][4 * r4 + e] * inv;
+        *reinterpret_cast<f32x4*>(dst + ct * 32 + r4 * 8) = val;
+      }
+  }
+}
+
 }  // namespace mgattn

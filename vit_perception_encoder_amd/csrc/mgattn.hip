@@ -49,13 +49,18 @@ int block_m_of(int d, int dtype) {
 // key steps).  A causal call keeps whole keys per wave: 128-query tiles of 4 waves.
 // Other kernels have one tile height.
 constexpr int kFillWorkgroups = 256;  // CUs of an MI355X
-enum class DenseKind { kFull8, kFull4, kSplit8, kSplit4, kOther };
+enum class DenseKind { kFull8, kFull4, kSplit8, kSplit4, kF32Split, kOther };
 int64_t dense_units(const int32_t* cu, int n_seg, int H, int bm) {
   int64_t units = 0;
   for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + bm - 1) / bm;
   return units * H;
 }
 DenseKind dense_kind(const int32_t* cu, int n_seg, int H, int d, int dtype, int causal) {
+  // f32: 32-query blocks with the keys split over the workgroup's waves when the
+  // 128-query tiles leave CUs idle (non-causal)
+  if (dtype == MGATTN_F32)
+    return !causal && dense_units(cu, n_seg, H, F32Tile<96>::kBlockM) < kFillWorkgroups ? DenseKind::kF32Split
+                                                                                         : DenseKind::kOther;
   if (dtype != MGATTN_BF16 || d != 96) return DenseKind::kOther;
   if (dense_units(cu, n_seg, H, 256) >= kFillWorkgroups) return DenseKind::kFull8;
   if (causal) return DenseKind::kFull4;
@@ -67,6 +72,7 @@ int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype, int cau
     case DenseKind::kFull4: return 128;
     case DenseKind::kSplit8: return 128;
     case DenseKind::kSplit4: return 64;
+    case DenseKind::kF32Split: return 32;
     default: return block_m_of(d, dtype);
   }
 }
@@ -78,11 +84,11 @@ long lds_bytes_of(int d, int dtype) {
       case 96: return sched::pipe_lds_elems<96>(256) * 2;  // the pipelined kernel, 256-query tiles
       case 128: return Bf16Tile<128>::kLdsBytes;
     }
-  } else {
+  } else {  // the larger of the two f32 workgroup shapes
     switch (d) {
-      case 64: return F32Tile<64>::kLdsBytes;
-      case 96: return F32Tile<96>::kLdsBytes;
-      case 128: return F32Tile<128>::kLdsBytes;
+      case 64: return std::max<long>(F32Tile<64>::kLdsBytes, f32_split_lds_bytes<64>());
+      case 96: return std::max<long>(F32Tile<96>::kLdsBytes, f32_split_lds_bytes<96>());
+      case 128: return std::max<long>(F32Tile<128>::kLdsBytes, f32_split_lds_bytes<128>());
     }
   }
   return MGATTN_ERR_HEAD_DIM;
@@ -336,6 +342,14 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
                        : launch_all(attn_fwd_bf16<128, false>, Bf16Tile<128>::kThreads, plan, args, s);
     }
   } else {
+    if (kind == DenseKind::kF32Split) {
+      switch (d) {
+        case 64: return launch_all(attn_fwd_f32_split<64, f32_split_waves<64>()>, f32_split_waves<64>() * 64, plan, args, s);
+        case 96: return launch_all(attn_fwd_f32_split<96, f32_split_waves<96>()>, f32_split_waves<96>() * 64, plan, args, s);
+        case 128:
+          return launch_all(attn_fwd_f32_split<128, f32_split_waves<128>()>, f32_split_waves<128>() * 64, plan, args, s);
+      }
+    }
     switch (d) {
       case 64: return launch_all(attn_fwd_f32<64>, F32Tile<64>::kThreads, plan, args, s);
       case 96: return launch_all(attn_fwd_f32<96>, F32Tile<96>::kThreads, plan, args, s);
