@@ -47,7 +47,7 @@ METRIC = "attention TFLOP/s (%bf16 MFMA peak) + ms per 50-layer tower attn @4096
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published 2.5 PFLOP/s): 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published 8 TB/s)
 THETA = 10000.0
-KERNEL_NAME = "attn_fwd_bf16_pipe<96, 8, false, false>"  # the dense head_dim-96 kernel the tower's layers launch (W, rope, key split)
+KERNEL_NAME = "attn_fwd_bf16_pipe<96, 8, false, 1>"  # the dense head_dim-96 kernel the tower's layers launch (W, rope, key groups)
 TRAFFIC_FILE = ROOT / "profiles" / "attn_fwd_bf16_pipe_96_tower4096_traffic.json"
 KERNEL_SOURCES = ["vit_perception_encoder_amd/csrc/attn_bf16_pipe.hpp", "vit_perception_encoder_amd/csrc/attn_bf16.hpp",
                   "vit_perception_encoder_amd/csrc/schedule.hpp", "vit_perception_encoder_amd/csrc/plan.hpp",

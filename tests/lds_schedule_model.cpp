@@ -204,12 +204,12 @@ static std::string pipe_case(int W, int kend) {
   return check(m);
 }
 
-// ---- the key-split pipelined kernel (attn_fwd_bf16_pipe<D, W, rope, true>): two wave
-// groups of W/2 waves, each wave one step (half a tile) per iteration; K and V rings
+// ---- the key-split pipelined kernel (attn_fwd_bf16_pipe<D, W, rope, NG>): NG wave
+// groups of W/NG waves, each wave one step (1/NG of a tile) per iteration; K and V rings
 template <int D>
-static std::string split_case(int W, int kend) {
+static std::string split_case(int W, int kend, int NG = 2) {
   using G = SplitGeometry<D>;
-  const int QB = W / 2, BM = 32 * QB, BN = G::kBlockN;
+  const int QB = W / NG, BM = 32 * QB, BN = G::kBlockN;
   const long KE = G::kKElems, VE = G::kVElems, OP = D + 8;
   const int ntiles = (kend + BN - 1) / BN, nsteps = ntiles;
   Model m;
@@ -221,13 +221,14 @@ static std::string split_case(int W, int kend) {
     K[t] = m.obj("K" + std::to_string(t), G::k_slot_elem(t), G::k_slot_elem(t) + KE);
     V[t] = m.obj("V" + std::to_string(t), G::v_slot_elem(t), G::v_slot_elem(t) + VE);
   }
-  // group 0's output staging rows, then group 1's partial results (13 x 64 x 16 bytes per wave)
-  std::vector<int> O(QB), P(QB);
+  // group 0's output staging rows, then the other groups' partial results (13 x 64 x 16
+  // bytes per wave), partial (g - 1) * QB + b for group g, query block b
+  std::vector<int> O(QB), P((NG - 1) * QB);
   const long part0 = QB * 32L * OP, part_elems = 13L * 64 * 8;
-  for (int b = 0; b < QB; ++b) {
-    O[b] = m.obj("O" + std::to_string(b), b * 32L * OP, (b + 1) * 32L * OP);
-    P[b] = m.obj("partial" + std::to_string(b), part0 + b * part_elems, part0 + (b + 1) * part_elems);
-  }
+  for (int b = 0; b < QB; ++b) O[b] = m.obj("O" + std::to_string(b), b * 32L * OP, (b + 1) * 32L * OP);
+  for (int i = 0; i < (NG - 1) * QB; ++i)
+    P[i] = m.obj("partial" + std::to_string(i), part0 + i * part_elems, part0 + (i + 1) * part_elems);
+  if (part0 + (NG - 1) * QB * part_elems > G::lds_elems(BM)) return "merge buffers outside the LDS";
   m.prog.resize(W);
   for (int w = 0; w < W; ++w) {
     auto& p = m.prog[w];
@@ -251,10 +252,10 @@ static std::string split_case(int W, int kend) {
       if (j >= 1) p.push_back({READ, V[split_v_tile(j)], 0});
     }
     p.push_back({BARRIER, -1, 0});
-    if (grp == 1) p.push_back({WRITE, P[qb], 0});
+    if (grp > 0) p.push_back({WRITE, P[(grp - 1) * QB + qb], 0});
     if (!mutated("split_merge_no_barrier")) p.push_back({BARRIER, -1, 0});
     if (grp == 0) {
-      p.push_back({READ, P[qb], 0});
+      for (int g = 1; g < NG; ++g) p.push_back({READ, P[(g - 1) * QB + qb], 0});
       p.push_back({WRITE, O[qb], 0});
     }
     if (mutated("split_merge_no_barrier")) p.push_back({BARRIER, -1, 0});
@@ -359,6 +360,7 @@ int main(int argc, char** argv) {
     else if ((r = pipe_case<96>(4, kend)).size()) what = "pipe<96, 4>";
     else if ((r = split_case<96>(8, kend)).size()) what = "pipe<96, 8, split>";
     else if ((r = split_case<96>(4, kend)).size()) what = "pipe<96, 4, split>";
+    else if ((r = split_case<96>(8, kend, 4)).size()) what = "pipe<96, 8, four groups>";
     else if ((r = phased_case<64>(kend)).size()) what = "phased<64>";
     else if ((r = phased_case<96>(kend)).size()) what = "phased<96>";
     else if ((r = phased_case<128>(kend)).size()) what = "phased<128>";
@@ -366,7 +368,7 @@ int main(int argc, char** argv) {
       printf("violation: %s, %d keys: %s\n", what, kend, r.c_str());
       return 1;
     }
-    cases += 7;
+    cases += 8;
   }
   printf("ok %ld\n", cases);
   return 0;

@@ -63,10 +63,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // Scheduling fence: the compiler moves no instruction across it.
 #define MGATTN_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <int D>
+// Slot plan of one iteration for steps of NB 32-key blocks: 64-key steps (NB = 2, every
+// shape but the four-group key split) or 32-key steps (NB = 1).
+template <int D, int NB = 2>
 struct PipeTile {
   using T = Bf16Tile<D>;
-  static constexpr int kNB = T::kStepKeys / 32;      // 32-key blocks per step
+  static constexpr int kNB = NB;                     // 32-key blocks per step
+  static constexpr int kStepKeys = 32 * kNB;
   static constexpr int kKS = D / 16;                 // QK k-steps
   static constexpr int kCT = D / 32;                 // 32-channel output tiles
   static constexpr int kNPV = kNB * 2 * kCT;         // PV MFMAs per iteration
@@ -85,21 +88,27 @@ struct PipeTile {
   static constexpr int qk_b(int i) { return i / kKS; }
   static constexpr int qk_s(int i) { return i % kKS; }
   // Softmax slices: slots 0..3 the row maxima, slot 4 the running maximum; score pair
-  // u (of the lane's 16: block u/8) is exponentiated in slot exp_slot(u) and converted
-  // to bf16 and summed one slot later; the row sum takes the step in slot kLSlot.
-  // Block 0's pairs end before slot kNPV and block 1's before kNPV + kKS; the
-  // conversions of block 0 start at slot kNPV/2, after PV(j-1) has read P block 0.
+  // u (of the lane's 16 NB: block u/8) is exponentiated in slot exp_slot(u) and
+  // converted to bf16 and summed one slot later; the row sum takes the step in slot
+  // kLSlot.  NB = 2: S and P have one buffer each; block 0's pairs end before slot kNPV
+  // and block 1's before kNPV + kKS, and the conversions of block 0 start at slot
+  // kNPV/2, after PV(j-1) has read P block 0.  NB = 1: S and P have two buffers,
+  // alternating by iteration parity, so the slices only follow the running maximum.
+  static constexpr int kBufs = kNB == 2 ? 1 : 2;
   static constexpr int exp_slot(int u) {
-    constexpr int tbl[16] = {5, 6, 7, 8, 9, 10, 11, 11, 12, 13, 13, 14, 15, 16, 16, 17};
-    return tbl[u];
+    constexpr int tbl2[16] = {5, 6, 7, 8, 9, 10, 11, 11, 12, 13, 13, 14, 15, 16, 16, 17};
+    constexpr int tbl1[8] = {5, 6, 7, 7, 8, 9, 9, 10};
+    return kNB == 2 ? tbl2[u] : tbl1[u];
   }
-  static constexpr int kLSlot = 19;
-  static_assert(D == 96, "the slot plan is laid out for head_dim 96 (12 PV + 12 QK MFMAs)");
-  static_assert(kNPV == 12 && kKS == 6 && kNSlot == 24, "slot plan");
+  static constexpr int kLSlot = kNB == 2 ? 19 : 11;
+  static_assert(D == 96, "the slot plan is laid out for head_dim 96 (6 k-steps, 3 channel tiles)");
+  static_assert(kKS == 6 && kNPV == 6 * kNB && kNSlot == 12 * kNB, "slot plan");
+  static_assert(kNB == 1 || kNB == 2, "32- or 64-key steps");
   static_assert(T::kStages == 3, "the pipelined loop needs three LDS stages");
-  static_assert(T::kBlockN == 2 * T::kStepKeys, "two softmax steps per LDS tile");
-  static_assert(kNB == 2, "the softmax slices assume two 32-key blocks per step");
+  static_assert(T::kBlockN == 2 * T::kStepKeys, "two 64-key steps per LDS tile");
   static_assert(kNPV >= kDK, "K reads start inside the PV slots");
+  static_assert(exp_slot(0) - 1 >= 4 && exp_slot(8 * kNB - 1) + 1 <= kLSlot && kLSlot < kNSlot,
+                "exponent arguments after the running maximum (slot 4), the row sum after the last conversion");
 };
 
 // W waves per workgroup, 32 queries each: 8 for launches that fill the chip, 4 (query
@@ -108,22 +117,25 @@ struct PipeTile {
 // rotation pairs are computed while the prologue's DMA is in flight, and the angles and
 // the rotation round exactly as the RoPE pass does (window_rope.hpp), so the result is
 // that of rotating q in memory first.
-// kSplit: the keys are split between two wave groups of W/2 waves (query tiles of
-// 16W), group g taking the second half of every 128-key tile when g = 1, each wave
-// running its own online softmax over its half; at the end group 1 hands its (m, l, O)
-// to group 0 through LDS, which merges them and stores the tile.  For launches whose
-// (segment, head, tile) units leave CUs idle: it halves the query tile and the steps
-// per wave.  Non-causal only.
-template <int D, int W, bool kRope = false, bool kSplit = false>
+// G > 1: the keys are split between G wave groups of W/G waves (query tiles of 32W/G),
+// group g taking keys g*128/G .. (g+1)*128/G - 1 of every 128-key tile (64-key steps
+// for two groups, 32-key steps for four), each wave running its own online softmax
+// over its part; at the end groups 1.. hand their (m, l, O) to group 0 through LDS,
+// which merges them and stores the tile.  For launches whose (segment, head, tile)
+// units leave CUs idle: smaller query tiles, fewer steps per wave.  Non-causal only.
+template <int D, int W, bool kRope = false, int G = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(W == 8 ? 2 : 1, 2)))
 void attn_fwd_bf16_pipe(KernelArgs a) {
+  static_assert(G == 1 || G == 2 || G == 4, "one, two or four key groups");
+  constexpr bool kSplit = G > 1;
   using TL = Bf16Tile<D>;
-  using PT = PipeTile<D>;
+  using PT = PipeTile<D, G == 4 ? 1 : 2>;
   using SG = sched::SplitGeometry<D>;
-  constexpr int G = kSplit ? 2 : 1;  // key groups
   constexpr int QB = W / G;          // 32-query blocks
+  static_assert(QB * G == W, "whole query blocks per group");
   constexpr int BM = 32 * QB, BN = TL::kBlockN;
-  constexpr int SK = TL::kStepKeys;
+  constexpr int SK = PT::kStepKeys;
+  static_assert(!kSplit || G * SK == BN, "the groups' steps tile a 128-key tile");
   constexpr int NB = PT::kNB, KS = PT::kKS, CT = PT::kCT;
   constexpr int NPV = PT::kNPV, NQK = PT::kNQK, NSLOT = PT::kNSlot;
   constexpr int DV = PT::kDV, DK = PT::kDK;
@@ -312,8 +324,12 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   float m_run = 0.0f, l_run = 0.0f, alpha = 1.0f;
   int resc = 0;  // O waits for the factor alpha (wave-uniform)
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  f32x16 s[NB];       // S(j) until the softmax has read it, then S(j+1)
-  bf16x8 p[NB][2];    // P(j-1) until PV(j-1) has read it, then P(j)
+  // NB = 2: one buffer, S(j) until the softmax has read it, then S(j+1), and P(j-1)
+  // until PV(j-1) has read it, then P(j).  NB = 1: iteration j reads S(j) and writes
+  // P(j) in buffer j % 2, QK(j+1) writes S(j+1) and PV(j-1) reads P(j-1) in the other.
+  constexpr int NBUF = PT::kBufs;
+  f32x16 s[NBUF][NB];
+  bf16x8 p[NBUF][NB][2];
 
   // K and V^T rows of this wave's step j.  Key-split: the ring offset goes through
   // readfirstlane, an opaque wave-uniform value, so the compiler forms each operand
@@ -346,8 +362,8 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     return *reinterpret_cast<const bf16x8*>(ks + (PT::qk_b(i) * 32 + n) * KP + 16 * PT::qk_s(i) + 8 * hf);
   };
 
-  // Scores of step j past the segment end or (causal) after the query: -inf.
-  auto mask = [&](int j) {
+  // Scores of step j (in buffer sb) past the segment end or (causal) after the query: -inf.
+  auto mask = [&](int j, f32x16 (&sb)[NB]) {
     const int key0 = kSplit ? j * BN + grp * SK : j * SK;
     if ((key0 + SK > L) || (a.causal && key0 + SK - 1 > qmin)) {
 #pragma unroll
@@ -355,23 +371,25 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + b * 32 + acc_row(r, hf);
-          if (key >= L || (a.causal && key > qr)) s[b][r] = -INFINITY;
+          if (key >= L || (a.causal && key > qr)) sb[b][r] = -INFINITY;
         }
     }
   };
 
   // One iteration.  HAS_PV: PV(j-1); HAS_QK: QK(j+1); HAS_SM: the softmax of step j;
-  // FIRST: the first softmax step (sets the running maximum).
-  auto iteration = [&](int j, auto has_pv, auto has_qk, auto has_sm, auto first) {
+  // FIRST: the first softmax step (sets the running maximum); PAR: j % 2 (NB = 1).
+  auto iteration = [&](int j, auto has_pv, auto has_qk, auto has_sm, auto first, auto par) {
     constexpr bool PV = decltype(has_pv)::value, QK = decltype(has_qk)::value;
     constexpr bool SM = decltype(has_sm)::value, FIRST = decltype(first)::value;
+    constexpr int BC = NBUF == 2 ? decltype(par)::value : 0;  // S(j) and P(j)
+    constexpr int BN1 = NBUF == 2 ? 1 - BC : 0;               // S(j+1) and P(j-1)
     if constexpr (PV) {
       if (resc) {  // the factor decided in the previous iteration, before PV(j-1) adds in
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
       }
     }
-    if constexpr (SM) mask(j);
+    if constexpr (SM) mask(j, s[BC]);
     const int jv = sched::pipe_v_step(j), jk = sched::pipe_k_step(j);
     const __bf16* vt = PV ? v_step(jv) : lds;
     const __bf16* ks = QK ? k_step(jk) : lds;
@@ -380,25 +398,26 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
     if constexpr (PV) {
       static_for<DV>([&](auto ic) { vf[decltype(ic)::value] = read_v(vt, decltype(ic)::value); });
     }
-    float mx[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // partial row maxima: block b, half h at 2b+h
+    float mx[2 * NB];              // partial row maxima: block b, half h at 2b+h
     float mc = 0.0f;
     float lsum[2] = {0.0f, 0.0f};  // two row-sum chains (even and odd score pairs)
-    float px[16][2];               // a score pair between its exponent argument and its conversion
+    float px[8 * NB][2];           // a score pair between its exponent argument and its conversion
     MGATTN_FENCE();
     static_for<NSLOT>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       // -- the MFMA of slot k
       if constexpr (k < NPV) {
         if constexpr (PV)
-          o[PT::pv_c(k)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k], p[PT::pv_b(k)][PT::pv_h(k)], o[PT::pv_c(k)],
-                                                                   0, 0, 0);
+          o[PT::pv_c(k)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[k], p[BN1][PT::pv_b(k)][PT::pv_h(k)],
+                                                                   o[PT::pv_c(k)], 0, 0, 0);
       } else {
         constexpr int i = k - NPV;
         if constexpr (QK) {
           if constexpr (PT::qk_s(i) == 0)
-            s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0], f32x16{}, 0, 0, 0);
+            s[BN1][PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[0], f32x16{}, 0, 0, 0);
           else
-            s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[PT::qk_s(i)], s[PT::qk_b(i)], 0, 0, 0);
+            s[BN1][PT::qk_b(i)] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[PT::qk_s(i)], s[BN1][PT::qk_b(i)], 0, 0, 0);
         }
       }
       // -- operand reads of later slots
@@ -406,21 +425,24 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
       if constexpr (QK && k + DK >= NPV && k + DK < NSLOT) kf[k + DK - NPV] = read_k(ks, k + DK - NPV);
       // -- the softmax slice of slot k
       if constexpr (SM) {
-        // slots 0..3: row maximum as four independent max3 chains over 8 scores each
+        // slots 0..3: row maximum as 2 NB independent max3 chains over 8 scores each
+        const f32x16(&sc)[NB] = s[BC];
         if constexpr (k < 4) {
-          static_for<4>([&](auto cc) {
+          static_for<2 * NB>([&](auto cc) {
             constexpr int ch = decltype(cc)::value, b = ch / 2, r0 = 8 * (ch % 2);
-            if constexpr (k == 0) mx[ch] = fmaxf(fmaxf(s[b][r0], s[b][r0 + 1]), s[b][r0 + 2]);
-            if constexpr (k == 1) mx[ch] = fmaxf(fmaxf(mx[ch], s[b][r0 + 3]), s[b][r0 + 4]);
-            if constexpr (k == 2) mx[ch] = fmaxf(fmaxf(mx[ch], s[b][r0 + 5]), s[b][r0 + 6]);
-            if constexpr (k == 3) mx[ch] = fmaxf(mx[ch], s[b][r0 + 7]);
+            if constexpr (k == 0) mx[ch] = fmaxf(fmaxf(sc[b][r0], sc[b][r0 + 1]), sc[b][r0 + 2]);
+            if constexpr (k == 1) mx[ch] = fmaxf(fmaxf(mx[ch], sc[b][r0 + 3]), sc[b][r0 + 4]);
+            if constexpr (k == 2) mx[ch] = fmaxf(fmaxf(mx[ch], sc[b][r0 + 5]), sc[b][r0 + 6]);
+            if constexpr (k == 3) mx[ch] = fmaxf(mx[ch], sc[b][r0 + 7]);
           });
         }
         if constexpr (k == 4) {
-          // a step with no visible key for some rows (causal) has maximum -inf; the
-          // floor keeps the reference finite (those rows get p = 0 and take alpha = 0
-          // at the first step with keys)
-          const float m_blk = fmaxf(half_swap_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))), -1.0e30f);
+          // a step with no visible key for some rows (causal, or a key group past the
+          // segment end) has maximum -inf; the floor keeps the reference finite (those
+          // rows get p = 0 and take alpha = 0 at the first step with keys)
+          float mxa = fmaxf(mx[0], mx[1]);
+          if constexpr (NB == 2) mxa = fmaxf(mxa, fmaxf(mx[2], mx[3]));
+          const float m_blk = fmaxf(half_swap_max(mxa), -1.0e30f);
           if constexpr (FIRST) {
             m_run = m_blk;
           } else {
@@ -435,14 +457,14 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
         // probabilities, pair by pair, in three stages one slot apart (no stage waits
         // on the one before it): exponent argument s*c - m*c, p = exp2, then the
         // conversion to bf16 (RNE) and the row sum
-        static_for<16>([&](auto uc) {
+        static_for<8 * NB>([&](auto uc) {
           constexpr int u = decltype(uc)::value;
           constexpr int b = u / 8, h2 = (u / 4) % 2, e = 2 * (u % 4);
           constexpr int E = PT::exp_slot(u);
           if constexpr (E + 1 == k) {
             const bf16x2 pr = {static_cast<__bf16>(px[u][0]), static_cast<__bf16>(px[u][1])};
-            p[b][h2][e] = pr[0];
-            p[b][h2][e + 1] = pr[1];
+            p[BC][b][h2][e] = pr[0];
+            p[BC][b][h2][e + 1] = pr[1];
             lsum[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[u & 1], false);
           }
           if constexpr (E == k) {
@@ -450,8 +472,8 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
             px[u][1] = __builtin_amdgcn_exp2f(px[u][1]);
           }
           if constexpr (E - 1 == k) {
-            px[u][0] = __builtin_fmaf(s[b][8 * h2 + e], c, -mc);
-            px[u][1] = __builtin_fmaf(s[b][8 * h2 + e + 1], c, -mc);
+            px[u][0] = __builtin_fmaf(sc[b][8 * h2 + e], c, -mc);
+            px[u][1] = __builtin_fmaf(sc[b][8 * h2 + e + 1], c, -mc);
           }
         });
         if constexpr (k == PT::kLSlot) {
@@ -488,6 +510,8 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
 
   using T_ = std::true_type;
   using F_ = std::false_type;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   // ---- S(0), then iteration 0 (no PV)
   {
     const __bf16* ks = k_step(0);
@@ -495,26 +519,43 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
       constexpr int i = decltype(ic)::value;
       const bf16x8 kf = read_k(ks, i);
       if constexpr (PT::qk_s(i) == 0)
-        s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], f32x16{}, 0, 0, 0);
+        s[0][PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], f32x16{}, 0, 0, 0);
       else
-        s[PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[PT::qk_s(i)], s[PT::qk_b(i)], 0, 0, 0);
+        s[0][PT::qk_b(i)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[PT::qk_s(i)], s[0][PT::qk_b(i)], 0, 0, 0);
     });
   }
   tile_sync(0);
-  if (nsteps > 1) iteration(0, F_{}, T_{}, T_{}, T_{});
-  else iteration(0, F_{}, F_{}, T_{}, T_{});
-  // ---- steady state: every part present
-  for (int j = 1; j + 1 < nsteps; ++j) {
-    tile_sync(j);
-    iteration(j, T_{}, T_{}, T_{}, F_{});
+  if (nsteps > 1) iteration(0, F_{}, T_{}, T_{}, T_{}, P0{});
+  else iteration(0, F_{}, F_{}, T_{}, T_{}, P0{});
+  // ---- steady state: every part present (two iterations per trip with two buffers)
+  int j = 1;
+  if constexpr (NBUF == 2) {
+    for (; j + 2 < nsteps; j += 2) {
+      tile_sync(j);
+      iteration(j, T_{}, T_{}, T_{}, F_{}, P1{});
+      tile_sync(j + 1);
+      iteration(j + 1, T_{}, T_{}, T_{}, F_{}, P0{});
+    }
+    if (j + 1 < nsteps) {
+      tile_sync(j);
+      iteration(j, T_{}, T_{}, T_{}, F_{}, P1{});
+      ++j;
+    }
+  } else {
+    for (; j + 1 < nsteps; ++j) {
+      tile_sync(j);
+      iteration(j, T_{}, T_{}, T_{}, F_{}, P0{});
+    }
   }
   // ---- the last softmax step (no QK), then PV of the last step
   if (nsteps > 1) {
     tile_sync(nsteps - 1);
-    iteration(nsteps - 1, T_{}, F_{}, T_{}, F_{});
+    if (NBUF == 2 && ((nsteps - 1) & 1)) iteration(nsteps - 1, T_{}, F_{}, T_{}, F_{}, P1{});
+    else iteration(nsteps - 1, T_{}, F_{}, T_{}, F_{}, P0{});
   }
   tile_sync(nsteps);
-  iteration(nsteps, T_{}, F_{}, F_{}, F_{});
+  if (NBUF == 2 && (nsteps & 1)) iteration(nsteps, T_{}, F_{}, F_{}, F_{}, P1{});
+  else iteration(nsteps, T_{}, F_{}, F_{}, F_{}, P0{});
   if (resc) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
@@ -527,36 +568,47 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   static_assert(QB * 32 * OP <= kLdsElems, "O staging must fit in the K/V stages");
   __syncthreads();
   if constexpr (kSplit) {
-    // group 1 hands each lane's (O, m, l) -- 13 float4, lane-major, after group 0's
+    // groups 1..G-1 hand each lane's (O, m, l) -- 13 float4, lane-major, after group 0's
     // staging rows -- to the group-0 wave of the same queries, which merges:
-    // m = max(m0, m1), O = O0 2^((m0-m)c) + O1 2^((m1-m)c), l likewise
+    // m = max_g m_g, O = sum_g O_g 2^((m_g-m)c), l likewise
     constexpr int kPart = CT * 4 + 1;
-    static_assert(QB * 32 * OP * 2 % 16 == 0 && QB * 32 * OP * 2 + QB * kPart * 64 * 16 <= kLdsElems * 2,
-                  "merge buffer must fit behind the staging rows");
-    f32x4* part = reinterpret_cast<f32x4*>(lds + QB * 32 * OP) + qb * kPart * 64 + lane;
-    if (grp == 1) {
+    static_assert(QB * 32 * OP * 2 % 16 == 0 && QB * 32 * OP * 2 + (G - 1) * QB * kPart * 64 * 16 <= kLdsElems * 2,
+                  "merge buffers must fit behind the staging rows");
+    f32x4* part = reinterpret_cast<f32x4*>(lds + QB * 32 * OP) + lane;
+    auto part_of = [&](int g) { return part + ((g - 1) * QB + qb) * kPart * 64; };
+    if (grp > 0) {
+      f32x4* pw = part_of(grp);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          part[(ct * 4 + r4) * 64] = f32x4{o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
-      part[CT * 4 * 64] = f32x4{m_run, l_run, 0.0f, 0.0f};
+          pw[(ct * 4 + r4) * 64] = f32x4{o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
+      pw[CT * 4 * 64] = f32x4{m_run, l_run, 0.0f, 0.0f};
     }
     __syncthreads();
-    if (grp == 1) return;
-    const f32x4 ml = part[CT * 4 * 64];
-    const float m_new = fmaxf(m_run, ml[0]);
+    if (grp > 0) return;
+    float m_new = m_run;
+#pragma unroll
+    for (int g = 1; g < G; ++g) m_new = fmaxf(m_new, part_of(g)[CT * 4 * 64][0]);
     const float f0 = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-    const float f1 = __builtin_amdgcn_exp2f((ml[0] - m_new) * c);
-    l_run = __builtin_fmaf(l_run, f0, ml[1] * f1);
+    l_run *= f0;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int ct = 0; ct < CT; ++ct) o[ct] *= f0;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 v1 = part[(ct * 4 + r4) * 64];
+    for (int g = 1; g < G; ++g) {
+      const f32x4* pg = part_of(g);
+      const f32x4 ml = pg[CT * 4 * 64];
+      const float fg = __builtin_amdgcn_exp2f((ml[0] - m_new) * c);
+      l_run = __builtin_fmaf(ml[1], fg, l_run);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[ct][4 * r4 + e] = __builtin_fmaf(o[ct][4 * r4 + e], f0, v1[e] * f1);
-      }
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 vg1 = pg[(ct * 4 + r4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[ct][4 * r4 + e] = __builtin_fmaf(vg1[e], fg, o[ct][4 * r4 + e]);
+        }
+    }
   }
   const float inv = 1.0f / half_swap_sum(l_run);
   __bf16* ow = lds + qb * 32 * OP;

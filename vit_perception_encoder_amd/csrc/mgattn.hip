@@ -43,13 +43,14 @@ int block_m_of(int d, int dtype) {
 // Workgroup shape of one dense call of the bf16 head_dim-96 kernel, which runs 8 or 4
 // waves of 32 queries: 256 queries (8 waves) when the (segment, head, tile) units give
 // at least one workgroup per CU.  With fewer, a non-causal call splits every tile's
-// keys between two wave groups (attn_fwd_bf16_pipe<.., true>): 128-query tiles of 8
-// waves when those fill the CUs, else 64-query tiles of 4 waves (a single 1024-token
-// segment of 16 heads: 64 units of 256, 256 units of 64, each wave taking 8 of the 16
-// key steps).  A causal call keeps whole keys per wave: 128-query tiles of 4 waves.
-// Other kernels have one tile height.
+// keys between wave groups (attn_fwd_bf16_pipe<.., G>): 128-query tiles of 8 waves in
+// two groups when those fill the CUs, else 64-query tiles of 8 waves in four groups,
+// each taking 32 keys of every 128 (a single 1024-token segment of 16 heads: 64 units
+// of 256, 256 units of 64, two waves per SIMD, 8 steps of 32 keys per wave).  A causal
+// call keeps whole keys per wave: 128-query tiles of 4 waves.  Other kernels have one
+// tile height.
 constexpr int kFillWorkgroups = 256;  // CUs of an MI355X
-enum class DenseKind { kFull8, kFull4, kSplit8, kSplit4, kF32Split, kOther };
+enum class DenseKind { kFull8, kFull4, kSplit8, kSplit4, kQuad8, kF32Split, kOther };
 int64_t dense_units(const int32_t* cu, int n_seg, int H, int bm) {
   int64_t units = 0;
   for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + bm - 1) / bm;
@@ -64,7 +65,7 @@ DenseKind dense_kind(const int32_t* cu, int n_seg, int H, int d, int dtype, int 
   if (dtype != MGATTN_BF16 || d != 96) return DenseKind::kOther;
   if (dense_units(cu, n_seg, H, 256) >= kFillWorkgroups) return DenseKind::kFull8;
   if (causal) return DenseKind::kFull4;
-  return dense_units(cu, n_seg, H, 128) >= kFillWorkgroups ? DenseKind::kSplit8 : DenseKind::kSplit4;
+  return dense_units(cu, n_seg, H, 128) >= kFillWorkgroups ? DenseKind::kSplit8 : DenseKind::kQuad8;
 }
 int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype, int causal) {
   switch (dense_kind(cu, n_seg, H, d, dtype, causal)) {
@@ -72,6 +73,7 @@ int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype, int cau
     case DenseKind::kFull4: return 128;
     case DenseKind::kSplit8: return 128;
     case DenseKind::kSplit4: return 64;
+    case DenseKind::kQuad8: return 64;
     case DenseKind::kF32Split: return 32;
     default: return block_m_of(d, dtype);
   }
@@ -330,11 +332,14 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
             return rope ? launch_all(attn_fwd_bf16_pipe<96, 4, true>, 4 * 64, plan, args, s)
                         : launch_all(attn_fwd_bf16_pipe<96, 4>, 4 * 64, plan, args, s);
           case DenseKind::kSplit8:
-            return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true, true>, 8 * 64, plan, args, s)
-                        : launch_all(attn_fwd_bf16_pipe<96, 8, false, true>, 8 * 64, plan, args, s);
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true, 2>, 8 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 8, false, 2>, 8 * 64, plan, args, s);
           case DenseKind::kSplit4:
-            return rope ? launch_all(attn_fwd_bf16_pipe<96, 4, true, true>, 4 * 64, plan, args, s)
-                        : launch_all(attn_fwd_bf16_pipe<96, 4, false, true>, 4 * 64, plan, args, s);
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 4, true, 2>, 4 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 4, false, 2>, 4 * 64, plan, args, s);
+          case DenseKind::kQuad8:
+            return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true, 4>, 8 * 64, plan, args, s)
+                        : launch_all(attn_fwd_bf16_pipe<96, 8, false, 4>, 8 * 64, plan, args, s);
           default: return MGATTN_ERR_HEAD_DIM;
         }
       case 128:
