@@ -231,9 +231,9 @@ int mgattn_dense_block_m(int d, int dtype);
  * refusals as mgattn_dense_plan), or a negative mgattn_status.  Pure host arithmetic.
  * The bf16 head_dim-96 kernel takes 256 when the (segment, head, q-tile) units of 256
  * give at least 256 workgroups (one per CU).  Otherwise a non-causal call splits each
- * tile's keys between two wave groups and takes 128 if the units of 128 give 256
- * workgroups, else 64 (one 1024-token segment of 16 heads: 64 units of 256, 256 of
- * 64); a causal call takes 128.  f32 takes 128, or 32 (the keys of each 32-query block
+ * tile's keys between wave groups and takes 128 (two groups) if the units of 128 give
+ * 256 workgroups, else 64 (four groups; one 1024-token segment of 16 heads: 64 units
+ * of 256, 256 of 64); a causal call takes 128.  f32 takes 128, or 32 (the keys of each 32-query block
  * split over the workgroup's waves) for a non-causal call whose 128-query units give
  * fewer than 256 workgroups.  Every other (d, dtype) has the single height of
  * mgattn_dense_block_m. */

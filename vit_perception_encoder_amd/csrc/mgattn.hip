@@ -50,7 +50,7 @@ int block_m_of(int d, int dtype) {
 // call keeps whole keys per wave: 128-query tiles of 4 waves.  Other kernels have one
 // tile height.
 constexpr int kFillWorkgroups = 256;  // CUs of an MI355X
-enum class DenseKind { kFull8, kFull4, kSplit8, kSplit4, kQuad8, kF32Split, kOther };
+enum class DenseKind { kFull8, kFull4, kSplit8, kQuad8, kF32Split, kOther };
 int64_t dense_units(const int32_t* cu, int n_seg, int H, int bm) {
   int64_t units = 0;
   for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + bm - 1) / bm;
@@ -72,7 +72,6 @@ int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype, int cau
     case DenseKind::kFull8: return 256;
     case DenseKind::kFull4: return 128;
     case DenseKind::kSplit8: return 128;
-    case DenseKind::kSplit4: return 64;
     case DenseKind::kQuad8: return 64;
     case DenseKind::kF32Split: return 32;
     default: return block_m_of(d, dtype);
@@ -334,9 +333,6 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
           case DenseKind::kSplit8:
             return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true, 2>, 8 * 64, plan, args, s)
                         : launch_all(attn_fwd_bf16_pipe<96, 8, false, 2>, 8 * 64, plan, args, s);
-          case DenseKind::kSplit4:
-            return rope ? launch_all(attn_fwd_bf16_pipe<96, 4, true, 2>, 4 * 64, plan, args, s)
-                        : launch_all(attn_fwd_bf16_pipe<96, 4, false, 2>, 4 * 64, plan, args, s);
           case DenseKind::kQuad8:
             return rope ? launch_all(attn_fwd_bf16_pipe<96, 8, true, 4>, 8 * 64, plan, args, s)
                         : launch_all(attn_fwd_bf16_pipe<96, 8, false, 4>, 8 * 64, plan, args, s);

@@ -83,10 +83,11 @@ constexpr MGATTN_HD int pipe_lds_elems(int bm) {
   return imax(Geometry<D>::kStages * Geometry<D>::kStageElems, pipe_q_elem<D>() + Geometry<D>::q_pad_elems(bm));
 }
 
-// ---- the key-split pipelined kernel (attn_fwd_bf16_pipe<D, W, R, true>), for launches
-// with too few (segment, head, query tile) units to fill the chip: two wave groups
-// share every 128-key tile, group g taking keys 64g .. 64g+63 of it, so a wave's step
-// j is half of tile j and each iteration consumes a whole tile.  Iteration j reads K
+// ---- the key-split pipelined kernel (attn_fwd_bf16_pipe<D, W, R, G> with G = 2 or 4
+// key groups), for launches with too few (segment, head, query tile) units to fill the
+// chip: the groups share every 128-key tile, group g taking keys g*128/G ..
+// (g+1)*128/G - 1 of it, so a wave's step j is that part of tile j and each iteration
+// consumes a whole tile.  Iteration j reads K
 // of tile j+1 (QK) and V of tile j-1 (PV); K tiles live in a ring of two slots, V
 // tiles in a ring of three, the Q tile after them.  Before QK(0): DMA of Q, K of tiles
 // 0 and 1 and V of tile 0, a wait for Q and K of tile 0, a barrier.  Every iteration j
