@@ -1,13 +1,17 @@
 """bench.py's contract that needs no GPU: one GPU only (refusal with a message for more),
-and the committed HBM-traffic summary is used only while the kernel sources it was
-taken on are unchanged."""
+the committed HBM-traffic summary is used only while the kernel sources it was taken
+on are unchanged, and the counter summaries that write profiles/ read rocprofv3's
+CSVs as intended."""
 from __future__ import annotations
 
+import csv
 import json
 import os
 import subprocess
 import sys
 from pathlib import Path
+
+import numpy as np
 
 ROOT = Path(__file__).resolve().parents[1]
 sys.path.insert(0, str(ROOT))
@@ -52,3 +56,61 @@ def test_traffic_summary_is_used_only_for_its_kernel_sources():
 def test_traffic_is_null_for_other_sources(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
     assert bench.traffic_per_launch() is None
+
+
+def _counter_csv(path, rows):
+    """A rocprofv3 counter_collection CSV: (dispatch id, kernel name, grid, counter, value)."""
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+            "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+            "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        for did, name, grid, counter, value in rows:
+            w.writerow([did, did, "Agent 1", 1, 1, 1, grid, 1, name, 512, 0, 0, 0, 0, 0, counter, value, 0, 1])
+
+
+def test_counter_summaries_on_synthetic_csv(tmp_path, monkeypatch):
+    """--write-traffic, --counter-table and --kernel-traffic on hand-made CSVs: counter
+    instances of a dispatch are summed, tower-shaped launches of the attention kernel
+    are picked by name and grid, the 1 GiB calibration copy sets the scale, and the
+    i-th tower launch is layer i mod 50 of the schedule."""
+    from vit_perception_encoder_amd import workloads as wl
+
+    att = f"void mgattn::{bench.KERNEL_NAME}(mgattn::KernelArgs)"
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # two counter instances per dispatch (summed): 3 tower launches of 24,000 KiB of FETCH,
+    # one launch of another grid, and the copy reading as 512 MiB (scale 2)
+    rows_f = []
+    for did in (1, 2, 3):
+        rows_f += [(did, att, bench.TOWER_GRID, "FETCH_SIZE", 12000.0)] * 2
+    rows_f += [(4, att, 65536, "FETCH_SIZE", 1.0), (5, bench.COPY_KERNEL, 1 << 20, "FETCH_SIZE", 524288.0)]
+    rows_w = [(did, att, bench.TOWER_GRID, "WRITE_SIZE", 12000.0) for did in (1, 2, 3)]
+    rows_w += [(5, bench.COPY_KERNEL, 1 << 20, "WRITE_SIZE", 1048576.0)]
+    _counter_csv(fetch, rows_f)
+    _counter_csv(write, rows_w)
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", tmp_path / "traffic.json")
+    assert bench.write_traffic(str(fetch), str(write)) == 0
+    t = json.loads((tmp_path / "traffic.json").read_text())
+    assert t["attention_dispatches"] == 3
+    assert t["calibration"]["fetch_scale"] == 2.0 and t["calibration"]["write_scale"] == 1.0
+    assert t["hbm_fetch_bytes_per_launch"] == 24000 * 1024 * 2
+    assert t["hbm_write_bytes_per_launch"] == 12000 * 1024
+    assert t["kernel_source_sha256"] == bench.kernel_source_hash()
+    # counter table: 52 tower launches, value = layer index; full layers average their indices
+    kinds = wl.tower_layer_kinds()
+    sq = tmp_path / "sq.csv"
+    _counter_csv(sq, [(i + 1, att, bench.TOWER_GRID, "SQ_WAVES", float(i % 50)) for i in range(52)])
+    r = _run(["--counter-table", str(sq)])
+    assert r.returncode == 0, r.stderr
+    line = next(x for x in r.stdout.splitlines() if x.startswith("| SQ_WAVES"))
+    idx = [i % 50 for i in range(52)]
+    want_full = np.mean([v for v in idx if kinds[v] == "full"])
+    want_win = np.mean([v for v in idx if kinds[v] == "window"])
+    got = [float(x) for x in line.strip("|").split("|")[1:]]
+    assert abs(got[0] - want_full) < 1e-3 * want_full and abs(got[1] - want_win) < 1e-3 * want_win
+    # kernel traffic: one row per (kernel, grid), scaled like write_traffic
+    r = _run(["--kernel-traffic", str(fetch), str(write)])
+    assert r.returncode == 0, r.stderr
+    tower_row = next(x for x in r.stdout.splitlines() if f"| {bench.TOWER_GRID} |" in x and "attn_fwd" in x)
+    assert "| 3 | 49.15 | 12.29 |" in tower_row, tower_row
