@@ -196,60 +196,67 @@ void attn_decode_bf16(KernelArgs a) {
   const float l_all = half_swap_sum(l_run);
 
   // ---- merge the eight partial results through LDS (the V buffers are dead once
-  // every wave has passed the barrier)
+  // every wave has passed the barrier).  Each wave stores its O tile as one float4 per
+  // lane and (output tile ct, register quad r4): slot [wave][ct][r4][lane], so a lane
+  // reads back the same four channels of the same query column from every wave, and
+  // the CT*4 slices are shared out over the waves.  Lane (n, hf) of slice (ct, r4)
+  // holds channels ct*32 + 8 r4 + 4 hf + [0, 4) of query column n.
   __syncthreads();
-  float* mf = reinterpret_cast<float*>(lds);
-  float* m_w = mf;                        // [wave][32]
-  float* l_w = mf + TL::kWaves * 32;      // [wave][32]
-  float* o_w = mf + TL::kWaves * 64;      // [wave][channel][32]
+  constexpr int NSL = CT * 4;                          // float4 slices per lane
+  f32x4* o_w = reinterpret_cast<f32x4*>(lds);          // [wave][NSL][64]
+  float* m_w = reinterpret_cast<float*>(o_w + TL::kWaves * NSL * 64);  // [wave][32]
+  float* l_w = m_w + TL::kWaves * 32;                  // [wave][32]
+  static_assert((TL::kWaves * NSL * 64 * 4 + TL::kWaves * 64) * 4 <= TL::kLdsBytes, "merge buffers inside LDS");
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      o_w[(wave * NSL + ct * 4 + r4) * 64 + lane] =
+          f32x4{o[ct][4 * r4], o[ct][4 * r4 + 1], o[ct][4 * r4 + 2], o[ct][4 * r4 + 3]};
   if (hf == 0) {
     m_w[wave * 32 + n] = m_run;
     l_w[wave * 32 + n] = l_all;
   }
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o_w[(wave * D + ct * 32 + acc_row(r, hf)) * 32 + n] = o[ct][r];
   __syncthreads();
-  // thread -> (query column, 8 consecutive channels); G*D/8 pieces
-  __bf16* og = static_cast<__bf16*>(a.o) + static_cast<size_t>(a.table.start[slot]) * a.ldo;
-  for (int piece = tid; piece < G * D / 8; piece += TL::kThreads) {
-    const int col = piece / (D / 8), ch0 = (piece % (D / 8)) * 8;
-    float M = -1.0e30f;
+  // weights of the eight waves for this lane's column: 2^{(m_w - M) c}, den = sum f_w l_w
+  float M = m_w[n];
 #pragma unroll
-    for (int w = 0; w < TL::kWaves; ++w) M = fmaxf(M, m_w[w * 32 + col]);
-    float den = 0.0f, f[TL::kWaves];
+  for (int w = 1; w < TL::kWaves; ++w) M = fmaxf(M, m_w[w * 32 + n]);
+  float f[TL::kWaves], den = 0.0f;
 #pragma unroll
-    for (int w = 0; w < TL::kWaves; ++w) {
-      f[w] = __builtin_amdgcn_exp2f((m_w[w * 32 + col] - M) * c);
-      den += f[w] * l_w[w * 32 + col];
+  for (int w = 0; w < TL::kWaves; ++w) {
+    f[w] = __builtin_amdgcn_exp2f((m_w[w * 32 + n] - M) * c);
+    den = __builtin_fmaf(f[w], l_w[w * 32 + n], den);
+  }
+  const bool col_ok = n < G;
+  __bf16* og = static_cast<__bf16*>(a.o) + static_cast<size_t>(a.table.start[slot]) * a.ldo +
+               static_cast<size_t>(g * G + n) * D + 4 * hf;
+  const size_t ps = static_cast<size_t>(wg) * nsplit + split;  // partial-result slot
+  // partial result of this split: O / den (0 for a split without keys), M, den
+  const float inv = nsplit == 1 ? 1.0f / den : (den > 0.0f ? 1.0f / den : 0.0f);
+  for (int sl = wave; sl < NSL; sl += TL::kWaves) {
+    f32x4 acc = o_w[sl * 64 + lane] * f[0];
+#pragma unroll
+    for (int w = 1; w < TL::kWaves; ++w) {
+      const f32x4 x = o_w[(w * NSL + sl) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(x[e], f[w], acc[e]);
     }
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[e] = 0.0f;
-#pragma unroll
-      for (int w = 0; w < TL::kWaves; ++w) acc[e] += f[w] * o_w[(w * D + ch0 + e) * 32 + col];
-    }
+    const int ch0 = (sl / 4) * 32 + (sl % 4) * 8;
+    if (!col_ok) continue;
     if (nsplit == 1) {
-      const float inv = 1.0f / den;
-      bf16x8 val;
+      bf16x4 val;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) val[e] = static_cast<__bf16>(acc[e] * inv);
-      *reinterpret_cast<bf16x8*>(og + static_cast<size_t>(g * G + col) * D + ch0) = val;
+      for (int e = 0; e < 4; ++e) val[e] = static_cast<__bf16>(acc[e] * inv);
+      *reinterpret_cast<bf16x4*>(og + ch0) = val;
     } else {
-      // partial result of this split: O / den (0 for a split without keys), M, den
-      const size_t ps = static_cast<size_t>(wg) * nsplit + split;
-      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-      f32x4* po = reinterpret_cast<f32x4*>(a.part + (ps * 32 + col) * D + ch0);
-      po[0] = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-      po[1] = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-      if (ch0 == 0) {
-        float* ml = a.part + static_cast<size_t>(a.table.n) * Hkv * nsplit * 32 * D + ps * 64;
-        ml[col] = M;
-        ml[32 + col] = den;
-      }
+      *reinterpret_cast<f32x4*>(a.part + (ps * 32 + n) * D + ch0 + 4 * hf) = acc * inv;
     }
+  }
+  if (nsplit > 1 && wave == 0 && hf == 0 && col_ok) {
+    float* ml = a.part + static_cast<size_t>(a.table.n) * Hkv * nsplit * 32 * D + ps * 64;
+    ml[n] = M;
+    ml[32 + n] = den;
   }
 }
 
