@@ -11,8 +11,9 @@ labelled uncertainties are now resolved").
 The 50 launches of a step are captured once into a HIP graph and replayed (--eager
 launches them from Python instead).  HIP events on the launch stream bracket the K
 timed steps; every launch inside is the attention kernel, so its average launch
-duration is the bracketed time over the launches.  A separate eager pass with events
-around each launch gives the full-layer / window-layer breakdown.
+duration is the bracketed time over the launches.  The full-layer / window-layer
+breakdown replays the layers of each kind as a graph of their own (time per launch),
+and an eager pass with events around each launch gives the same split as "ms_events".
 
 Prints ONE JSON line: algorithmic TFLOP/s over the whole step (4*S^2*d*H per
 segment), ms per step (= ms per tower), the roofline of the attention kernel, and
@@ -46,6 +47,7 @@ sys.path.insert(0, str(ROOT))
 METRIC = "attention TFLOP/s (%bf16 MFMA peak) + ms per 50-layer tower attn @4096 tok"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (published 2.5 PFLOP/s): 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published 8 TB/s)
+PEAK_F32_TFLOPS = 157.3    # MI355X dense f32 (published 157.3 TFLOP/s), the f32 path's own peak
 THETA = 10000.0
 KERNEL_NAME = "attn_fwd_bf16_pipe<96, 8, false, 1>"  # the dense head_dim-96 kernel the tower's layers launch (W, rope, key groups)
 TRAFFIC_FILE = ROOT / "profiles" / "attn_fwd_bf16_pipe_96_tower4096_traffic.json"
@@ -350,9 +352,12 @@ def tower_448(torch, mg, wl, reps: int = 10) -> dict:
 
 
 def config_times(torch, mg, wl):
-    """Each parity workload timed on its own (events around each launch, median): the
-    f32 256-token segment, the 1024-token full layer, the 4 x 1024 window layer, and the
-    ragged batches' full and window layers (17,408 and 16,384 tokens)."""
+    """Each parity workload timed on its own: the f32 256-token segment, the 1024-token
+    full layer, the 4 x 1024 window layer, and the ragged batches' full and window
+    layers (17,408 and 16,384 tokens).  "ms": per call of 20 calls replayed as one HIP
+    graph (kernel time plus the gaps between launches; the inputs stay in the caches
+    between calls); "ms_events": events around single launches, median (adds the host
+    enqueue gap).  The rate and fraction use "ms" and the peak of the case's own dtype."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     cases = [wl.config_tiny(), wl.config_full448(), wl.config_window896()]
@@ -367,11 +372,16 @@ def config_times(torch, mg, wl):
             q, k, v = (torch.from_numpy(x).to(dev) for x in (c.q, c.k, c.v))
         out = torch.empty_like(q)
         cu = [int(x) for x in c.cu_seqlens]
-        ms = time_launches(torch, lambda: mg.mgattn_dense(q, k, v, out, cu, c.n_seg, c.H, c.d, c.scale, c.causal,
-                                                          c.dtype, stream))
+        def call(s, q=q, k=k, v=v, out=out, cu=cu, c=c):
+            mg.mgattn_dense(q, k, v, out, cu, c.n_seg, c.H, c.d, c.scale, c.causal, c.dtype, s)
+
+        ms_e = time_launches(torch, lambda: call(stream))
+        ms = time_graph(torch, call)
         fl = c.flops()
-        res[c.name] = {"ms": ms, "tokens": c.T, "segments": c.n_seg, "dtype": "bf16" if c.dtype == wl.BF16 else "f32",
-                       "tflops": fl / (ms * 1e-3) / 1e12, "frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        peak = PEAK_BF16_TFLOPS if c.dtype == wl.BF16 else PEAK_F32_TFLOPS
+        res[c.name] = {"ms": ms, "ms_events": ms_e, "tokens": c.T, "segments": c.n_seg,
+                       "dtype": "bf16" if c.dtype == wl.BF16 else "f32", "peak_tflops": peak,
+                       "tflops": fl / (ms * 1e-3) / 1e12, "frac": fl / (ms * 1e-3) / 1e12 / peak}
     return res
 
 
@@ -700,7 +710,7 @@ def main() -> int:
     flops_per_launch = step_flops / len(layers)
     achieved = flops_per_launch / (launch_ms_mean * 1e-3) / 1e12
 
-    # per-layer-kind breakdown: a separate eager pass with events around each launch
+    # per-layer-kind breakdown, events around each launch of an eager pass
     nb = max(3, min(args.steps, 10))
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers] for _ in range(nb)]
     for s_ in range(nb):
@@ -710,8 +720,18 @@ def main() -> int:
                            for s_ in range(nb)])
     full_idx = [i for i, x in enumerate(layers) if x[6] == "full"]
     win_idx = [i for i, x in enumerate(layers) if x[6] == "window"]
-    full_ms = float(np.median(per_launch[:, full_idx]))
-    win_ms = float(np.median(per_launch[:, win_idx]))
+    full_ms_e = float(np.median(per_launch[:, full_idx]))
+    win_ms_e = float(np.median(per_launch[:, win_idx]))
+    # the same split as the tower graph runs it: the layers of one kind (each on its own
+    # inputs) captured into one graph and replayed, time per launch
+    def kind_ms(idx):
+        def one_pass(strm):
+            for i in idx:
+                q, k, v, cu, nseg, _, _ = layers[i]
+                mg.mgattn_dense(q, k, v, out, cu, nseg, wl.HEADS, wl.HEAD_DIM, wl.SCALE, 0, mg.MGATTN_BF16, strm)
+        return time_graph(torch, one_pass, n=1) / len(idx)
+
+    full_ms, win_ms = kind_ms(full_idx), kind_ms(win_idx)
     full_tf = layers[full_idx[0]][5] / (full_ms * 1e-3) / 1e12
     win_tf = layers[win_idx[0]][5] / (win_ms * 1e-3) / 1e12
 
@@ -769,8 +789,10 @@ def main() -> int:
         "detail": {
             "tower_ms": ms_per_step,
             "frac_of_bf16_peak": step_flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "full_layer_4096": {"ms": full_ms, "tflops": full_tf, "frac": full_tf / PEAK_BF16_TFLOPS},
-            "window_layer_4x1024": {"ms": win_ms, "tflops": win_tf, "frac": win_tf / PEAK_BF16_TFLOPS},
+            "full_layer_4096": {"ms": full_ms, "ms_events": full_ms_e, "tflops": full_tf,
+                                "frac": full_tf / PEAK_BF16_TFLOPS, "launches": len(full_idx)},
+            "window_layer_4x1024": {"ms": win_ms, "ms_events": win_ms_e, "tflops": win_tf,
+                                    "frac": win_tf / PEAK_BF16_TFLOPS, "launches": len(win_idx)},
             "step_gflop": step_flops / 1e9,
             "wall_s_timed_region": wall,
             "oracle_parity_full_layers_max_abs_err": parity,
