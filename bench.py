@@ -427,22 +427,27 @@ def token_path(torch, mg, wl, layers):
     for lname, li in (("full_layer_4096", 3), ("window_layer_4x1024", 0)):
         cu_l, nseg_l, fl_l = layers[li][3], layers[li][4], layers[li][5]
 
-        def unfused():
-            mg.mgattn_rope2d(qkv[:, :2 * row], qkv.stride(0), grid64, 32, 2 * H, d, THETA, mg.MGATTN_BF16, stream)
+        def unfused(s, cu_l=cu_l, nseg_l=nseg_l):
+            mg.mgattn_rope2d(qkv[:, :2 * row], qkv.stride(0), grid64, 32, 2 * H, d, THETA, mg.MGATTN_BF16, s)
             mg.mgattn_dense_strided(qkv[:, :row], qkv[:, row:2 * row], qkv[:, 2 * row:], out, qkv.stride(0),
                                     qkv.stride(0), qkv.stride(0), row, cu_l, nseg_l, H, d, wl.SCALE, 0, mg.MGATTN_BF16,
-                                    stream)
+                                    s)
 
-        def fused():
+        def fused(s, cu_l=cu_l, nseg_l=nseg_l):
             mg.mgattn_dense_rope2d(qkv[:, :row], qkv[:, row:2 * row], qkv[:, 2 * row:], out, qkv.stride(0),
                                    qkv.stride(0), qkv.stride(0), row, cu_l, nseg_l, H, d, wl.SCALE, 0, mg.MGATTN_BF16,
-                                   grid64, 32, THETA, stream)
+                                   grid64, 32, THETA, s)
 
+        # alternation, three rounds, best of each: "ms" per call from a graph of 20
+        # calls, "ms_events" with events around one call's launches
         bt = {"unfused": float("inf"), "fused": float("inf")}
+        be = dict(bt)
         for _ in range(3):
             for name, fn in (("unfused", unfused), ("fused", fused)):
-                bt[name] = min(bt[name], time_launches(torch, fn))
+                bt[name] = min(bt[name], time_graph(torch, fn))
+                be[name] = min(be[name], time_launches(torch, lambda fn=fn: fn(stream)))
         res[f"rope_attention_{lname}"] = {"unfused_ms": bt["unfused"], "fused_ms": bt["fused"],
+                                          "unfused_ms_events": be["unfused"], "fused_ms_events": be["fused"],
                                           "fused_tflops": fl_l / (bt["fused"] * 1e-3) / 1e12}
     # the HBM-bound kernels: "ms" from a graph of 20 calls (per call), "ms_events" with
     # events around single launches (host launch overhead included)
