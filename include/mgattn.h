@@ -220,7 +220,8 @@ int mgattn_dense_supported(int H, int d, int dtype);
  * for, or a negative mgattn_status if (d, dtype) is not supported.  Pure host
  * arithmetic, no GPU needed; equals the static LDS footprint of the kernel's largest
  * workgroup shape (bf16 head_dim 96: the 256-query tile; f32: the key-split 32-query
- * block at head_dim 64 and 96, the 128-query tile at 128). */
+ * block at head_dim 64 and 96, the 128-query tile at 128; the key-split 16-query block
+ * asks for less at every head_dim). */
 long mgattn_dense_lds_bytes(int d, int dtype);
 
 /* Queries per workgroup of the (d, dtype) kernel (the tallest q-tile it uses), or a
@@ -233,10 +234,11 @@ int mgattn_dense_block_m(int d, int dtype);
  * give at least 256 workgroups (one per CU).  Otherwise a non-causal call splits each
  * tile's keys between wave groups and takes 128 (two groups) if the units of 128 give
  * 256 workgroups, else 64 (four groups; one 1024-token segment of 16 heads: 64 units
- * of 256, 256 of 64); a causal call takes 128.  f32 takes 128, or 32 (the keys of each 32-query block
- * split over the workgroup's waves) for a non-causal call whose 128-query units give
- * fewer than 256 workgroups.  Every other (d, dtype) has the single height of
- * mgattn_dense_block_m. */
+ * of 256, 256 of 64); a causal call takes 128.  f32 takes 128, or for a non-causal
+ * call whose 128-query units give fewer than 256 workgroups 32 (the keys of each
+ * 32-query block split over the workgroup's waves), or 16 if the 32-query blocks too
+ * give fewer than 256 (a 256-token segment of 16 heads: 128 blocks of 32, 256 of 16).
+ * Every other (d, dtype) has the single height of mgattn_dense_block_m. */
 int mgattn_dense_plan_block_m(const int32_t* cu_seqlens, int n_seg, int H, int d, int dtype, int causal);
 
 /* Introspection of the work split (pure host arithmetic, no GPU needed).

@@ -61,10 +61,12 @@ def test_lds_bytes_arithmetic(lib):
         stage = (128 * (d + 8) + 128 * d) * 2
         stages = 3 if 3 * stage <= 160 * 1024 else 2
         want_bf16 = stages * stage if d != 96 else max(3 * stage, 2 * stage + 256 * (d + 8) * 2)
-        # f32: the larger of 128-query tiles (two stages of 32-key K and V tiles, pitch
-        # d+4) and the key-split 32-query blocks ((W-1) waves' partial results of d/32*4+1
-        # float4 per lane, W = 8, or 4 at d = 128)
-        want_f32 = max(2 * 2 * 32 * (d + 4) * 4, ((4 if d == 128 else 8) - 1) * (d // 32 * 4 + 1) * 64 * 16)
+        # f32: the largest of 128-query tiles (two stages of 32-key K and V tiles, pitch
+        # d+4), the key-split 32-query blocks ((W-1) waves' partial results of d/32*4+1
+        # float4 per lane, W = 8, or 4 at d = 128) and the key-split 16-query blocks
+        # (7 waves' partial results of d/16+1 float4 per lane)
+        want_f32 = max(2 * 2 * 32 * (d + 4) * 4, ((4 if d == 128 else 8) - 1) * (d // 32 * 4 + 1) * 64 * 16,
+                       7 * (d // 16 + 1) * 64 * 16)
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_BF16) == want_bf16
         assert mg.mgattn_dense_lds_bytes(d, mg.MGATTN_F32) == want_f32
         assert want_bf16 <= 160 * 1024 and want_f32 <= 160 * 1024
@@ -193,8 +195,8 @@ def test_plan_is_a_bijection(lib, cu, H, dtype, causal):
     ([0, 1024, 2048, 3072, 4096], 16, 256, 256, 128),  # its window layer
     ([0, 1024], 16, 64, 128, 32),         # one 448x448 image: 64 units of 256, 256 of 64 (key-split)
     ([0, 2048], 16, 128, 128, 128),       # 128 units of 256, 256 of 128 (key-split)
-    ([0, 256], 16, 64, 128, 32),          # the f32 workload: 32 units of 128 (f32 key split)
-    ([0, 100], 1, 64, 128, 32),           # nothing fills the chip: the shortest tile
+    ([0, 256], 16, 64, 128, 16),          # the f32 workload: 32 units of 128, 128 of 32 (f32 key split)
+    ([0, 100], 1, 64, 128, 16),           # nothing fills the chip: the shortest tile
     ([0, 1024] + [1024 + 64 * i for i in range(1, 49)], 16, 256, 256, 128),  # 49 segments x 16 heads
 ])
 def test_plan_block_m_fills_the_chip(lib, cu, H, want, want_causal, want_f32):
@@ -202,7 +204,7 @@ def test_plan_block_m_fills_the_chip(lib, cu, H, want, want_causal, want_f32):
     for causal, bm in ((0, want), (1, want_causal)):
         assert mg.mgattn_dense_plan_block_m(cu, n, H, 96, 1, causal) == bm
         assert mg.mgattn_dense_plan_block_m(cu, n, H, 64, 1, causal) == 256  # one tile height at d = 64
-        # f32: 128-query tiles, or 32-query key-split blocks for a short non-causal call
+        # f32: 128-query tiles, or 32- or 16-query key-split blocks for a short non-causal call
         assert mg.mgattn_dense_plan_block_m(cu, n, H, 96, 0, causal) == (want_f32 if not causal else 128)
         assert sum(mg.mgattn_dense_plan(cu, n, H, 96, 1, causal)) == H * sum(
             -(-(cu[g + 1] - cu[g]) // bm) for g in range(n))

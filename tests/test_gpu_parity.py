@@ -155,14 +155,16 @@ def test_key_split_large_logits(torch):
     _full_check(torch, case)
 
 
-def test_f32_key_split_long_segments(torch):
-    """f32 calls too short to fill the chip run 32-query blocks with the keys split over
-    eight waves (four at head_dim 128): long segments give every wave several 32-key
-    tiles, short ones leave waves without tiles; keys scaled x4 so the waves' maxima
-    differ.  Tolerance 1e-4 (f32)."""
-    for d in (96, 128):
-        case = _rand_case(f"f32_split_d{d}", [2047, 33, 1, 0, 64], H=2, d=d, dtype=wl.F32, seed=18, kscale=4.0)
-        assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, 2, d, wl.F32, 0) == 32
+@pytest.mark.parametrize("H,bm", [(8, 32), (2, 16)])
+def test_f32_key_split_long_segments(torch, H, bm):
+    """f32 calls too short to fill the chip run 32-query blocks (eight heads: 552 of
+    them) or, when those leave CUs idle too, 16-query blocks (two heads: 138 blocks of
+    32) with the keys split over eight waves (four at head_dim 128 with 32-query
+    blocks): long segments give every wave several 32-key tiles, short ones leave waves
+    without tiles; keys scaled x4 so the waves' maxima differ.  Tolerance 1e-4 (f32)."""
+    for d in (64, 96, 128):
+        case = _rand_case(f"f32_split{bm}_d{d}", [2047, 33, 1, 0, 64], H=H, d=d, dtype=wl.F32, seed=18, kscale=4.0)
+        assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, H, d, wl.F32, 0) == bm
         _full_check(torch, case)
 
 

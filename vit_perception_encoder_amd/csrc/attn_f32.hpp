@@ -383,4 +383,193 @@ void attn_fwd_f32_split(KernelArgs a) {
   }
 }
 
+// Exchange with lane l^16 and combine (max or sum) -- one v_permlane16_swap: rows of 16
+// lanes 0 <-> 1 and 2 <-> 3.
+__device__ inline float row16_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float row16_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The same key split with one 16-query block per workgroup, for calls whose 32-query
+// blocks still leave CUs idle (a 256-token segment of 16 heads is 128 blocks of 32, 256
+// of 16): twice the workgroups, half the products per CU.  v_mfma_f32_16x16x4_f32, lane
+// l = 16 g + n (lane group g, column n).  S^T = K Q^T per 16-key block: step s contracts
+// channel g*D/4 + s (each lane group supplies a contiguous quarter of the row, so a lane
+// reads a contiguous quarter row of K and Q), and the accumulator holds keys 4g + r
+// (r = 0..3) of the block for query n.  O^T += V^T P^T per 32-key tile in 8 steps:
+// step (b, r) contracts key 16b + 4g + r, whose probability lane (g, n) holds in its own
+// register (b, r), so P never leaves its lane; the A operand is V[key][16ct + n].  The
+// row maximum combines the four lane groups with two lane swaps (16, then 32), the row
+// sum once at the end.  Waves take the 32-key tiles t = wave, wave + W, ...; waves
+// 1..W-1 hand (m, l, O) to wave 0 through LDS, as in attn_fwd_f32_split.
+template <int D>
+constexpr int f32_split16_waves() { return 8; }
+template <int D>
+constexpr long f32_split16_lds_bytes() { return (f32_split16_waves<D>() - 1) * (D / 16 + 1) * 64 * 16L; }
+
+template <int D, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_f32_split16(KernelArgs a) {
+  constexpr int BM = 16, BN = 32;
+  constexpr int QD = D / 4;      // channels per lane group = QK steps per 16-key block
+  constexpr int CT = D / 16;     // 16-channel output tiles
+  constexpr int kPart = CT + 1;  // float4 per lane: O, then (m, l)
+  constexpr float kRescaleLog2 = 8.0f;
+  static_assert(QD % 4 == 0, "a lane group's quarter row is whole float4 pieces");
+  __shared__ __attribute__((aligned(16))) f32x4 part[(W - 1) * kPart * 64];
+  static_assert(W == f32_split16_waves<D>() && sizeof(part) == f32_split16_lds_bytes<D>(), "LDS bytes the host reports");
+
+  const Tile tile = decode_tile(a.table, a.H, BM, 0, blockIdx.x);
+  if (!tile.valid) return;
+  const int L = a.table.len[tile.slot];  // queries = keys of the segment
+  const int q0 = tile.q0;
+  const size_t t0 = static_cast<size_t>(a.table.start[tile.slot]);
+  const size_t hoff = static_cast<size_t>(tile.head) * D;
+  const float* __restrict__ qg = static_cast<const float*>(a.q) + t0 * a.ldq + hoff;
+  const float* __restrict__ kg = static_cast<const float*>(a.k) + t0 * a.ldk + hoff;
+  const float* __restrict__ vg = static_cast<const float*>(a.v) + t0 * a.ldv + hoff;
+  float* __restrict__ og = static_cast<float*>(a.o) + t0 * a.ldo + hoff;
+
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;  // query column
+  const int g = lane >> 4;  // lane group
+  const float c = a.c;
+  const int qr = q0 + n;
+
+  float qf[QD];
+  if (qr < L) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(qg + static_cast<size_t>(qr) * a.ldq + g * QD);
+#pragma unroll
+    for (int j = 0; j < QD / 4; ++j) {
+      const f32x4 x = p[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf[4 * j + e] = x[e] * static_cast<float>(a.qsign);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < QD; ++j) qf[j] = 0.0f;
+  }
+
+  const int ntiles = (L + BN - 1) / BN;
+  f32x4 o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  for (int t = wave; t < ntiles; t += W) {
+    const int kt0 = t * BN;
+    // K rows kt0 + 16b + n (rows past the segment end read as zeros), channels g*QD + [0, QD)
+    f32x4 kq[2][QD / 4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const bool krow = kt0 + 16 * b + n < L;
+      const f32x4* kp = reinterpret_cast<const f32x4*>(kg + static_cast<size_t>(kt0 + 16 * b + n) * a.ldk + g * QD);
+#pragma unroll
+      for (int j = 0; j < QD / 4; ++j) kq[b][j] = krow ? kp[j] : f32x4{};
+    }
+    // V elements (key kt0 + 16b + 4g + r, channel 16ct + n)
+    float vv[2][4][CT];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kt0 + 16 * b + 4 * g + r;
+        const float* vr = vg + static_cast<size_t>(key) * a.ldv + n;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) vv[b][r][ct] = key < L ? vr[16 * ct] : 0.0f;
+      }
+    f32x4 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x4{};
+#pragma unroll
+      for (int j = 0; j < QD / 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(kq[b][j][e], qf[4 * j + e], s[b], 0, 0, 0);
+    }
+    const bool masked = kt0 + BN > L;
+    if (masked) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kt0 + 16 * b + 4 * g + r >= L) s[b][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+    mx = fmaxf(mx, fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    const float m_tile = fmaxf(half_swap_max(row16_swap_max(mx)), -1.0e30f);
+    if (t == wave) {
+      m_run = m_tile;
+    } else if (__builtin_amdgcn_ballot_w64((m_tile - m_run) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+    }
+    const float mc = m_run * c;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][r], c, -mc));
+        if (masked && kt0 + 16 * b + 4 * g + r >= L) p = 0.0f;
+        s[b][r] = p;
+        lsum += p;
+      }
+    l_run += lsum;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[b][r][ct], s[b][r], o[ct], 0, 0, 0);
+  }
+
+  // merge: a wave without tiles holds m = -inf, l = 0, O = 0 and weighs nothing
+  if (wave > 0) {
+    f32x4* pw = part + (wave - 1) * kPart * 64 + lane;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) pw[ct * 64] = o[ct];
+    pw[CT * 64] = f32x4{m_run, l_run, 0.0f, 0.0f};
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  float m_all = m_run;
+#pragma unroll
+  for (int w = 1; w < W; ++w) m_all = fmaxf(m_all, part[(w - 1) * kPart * 64 + CT * 64 + lane][0]);
+  const float f0 = __builtin_amdgcn_exp2f((m_run - m_all) * c);
+  l_run *= f0;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] *= f0;
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    const f32x4* pw = part + (w - 1) * kPart * 64 + lane;
+    const f32x4 ml = pw[CT * 64];
+    const float fw = __builtin_amdgcn_exp2f((ml[0] - m_all) * c);
+    l_run = __builtin_fmaf(ml[1], fw, l_run);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const f32x4 v = pw[ct * 64];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[ct][e] = __builtin_fmaf(v[e], fw, o[ct][e]);
+    }
+  }
+  // the row sum over the four lane groups' keys
+  const float inv = 1.0f / half_swap_sum(row16_swap_sum(l_run));
+  if (qr < L) {
+    float* dst = og + static_cast<size_t>(qr) * a.ldo + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4*>(dst + 16 * ct) = o[ct] * inv;
+  }
+}
+
+
 }  // namespace mgattn

@@ -50,7 +50,7 @@ int block_m_of(int d, int dtype) {
 // call keeps whole keys per wave: 128-query tiles of 4 waves.  Other kernels have one
 // tile height.
 constexpr int kFillWorkgroups = 256;  // CUs of an MI355X
-enum class DenseKind { kFull8, kFull4, kSplit8, kQuad8, kF32Split, kOther };
+enum class DenseKind { kFull8, kFull4, kSplit8, kQuad8, kF32Split, kF32Split16, kOther };
 int64_t dense_units(const int32_t* cu, int n_seg, int H, int bm) {
   int64_t units = 0;
   for (int g = 0; g < n_seg; ++g) units += (static_cast<int64_t>(cu[g + 1] - cu[g]) + bm - 1) / bm;
@@ -58,10 +58,11 @@ int64_t dense_units(const int32_t* cu, int n_seg, int H, int bm) {
 }
 DenseKind dense_kind(const int32_t* cu, int n_seg, int H, int d, int dtype, int causal) {
   // f32: 32-query blocks with the keys split over the workgroup's waves when the
-  // 128-query tiles leave CUs idle (non-causal)
-  if (dtype == MGATTN_F32)
-    return !causal && dense_units(cu, n_seg, H, F32Tile<96>::kBlockM) < kFillWorkgroups ? DenseKind::kF32Split
-                                                                                         : DenseKind::kOther;
+  // 128-query tiles leave CUs idle (non-causal), 16-query blocks when those do too
+  if (dtype == MGATTN_F32) {
+    if (causal || dense_units(cu, n_seg, H, F32Tile<96>::kBlockM) >= kFillWorkgroups) return DenseKind::kOther;
+    return dense_units(cu, n_seg, H, 32) >= kFillWorkgroups ? DenseKind::kF32Split : DenseKind::kF32Split16;
+  }
   if (dtype != MGATTN_BF16 || d != 96) return DenseKind::kOther;
   if (dense_units(cu, n_seg, H, 256) >= kFillWorkgroups) return DenseKind::kFull8;
   if (causal) return DenseKind::kFull4;
@@ -74,6 +75,7 @@ int dense_block_m(const int32_t* cu, int n_seg, int H, int d, int dtype, int cau
     case DenseKind::kSplit8: return 128;
     case DenseKind::kQuad8: return 64;
     case DenseKind::kF32Split: return 32;
+    case DenseKind::kF32Split16: return 16;
     default: return block_m_of(d, dtype);
   }
 }
@@ -85,11 +87,12 @@ long lds_bytes_of(int d, int dtype) {
       case 96: return sched::pipe_lds_elems<96>(256) * 2;  // the pipelined kernel, 256-query tiles
       case 128: return Bf16Tile<128>::kLdsBytes;
     }
-  } else {  // the larger of the two f32 workgroup shapes
+  } else {  // the largest of the three f32 workgroup shapes
     switch (d) {
-      case 64: return std::max<long>(F32Tile<64>::kLdsBytes, f32_split_lds_bytes<64>());
-      case 96: return std::max<long>(F32Tile<96>::kLdsBytes, f32_split_lds_bytes<96>());
-      case 128: return std::max<long>(F32Tile<128>::kLdsBytes, f32_split_lds_bytes<128>());
+      case 64: return std::max({F32Tile<64>::kLdsBytes + 0L, f32_split_lds_bytes<64>(), f32_split16_lds_bytes<64>()});
+      case 96: return std::max({F32Tile<96>::kLdsBytes + 0L, f32_split_lds_bytes<96>(), f32_split16_lds_bytes<96>()});
+      case 128:
+        return std::max({F32Tile<128>::kLdsBytes + 0L, f32_split_lds_bytes<128>(), f32_split16_lds_bytes<128>()});
     }
   }
   return MGATTN_ERR_HEAD_DIM;
@@ -343,6 +346,13 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
                        : launch_all(attn_fwd_bf16<128, false>, Bf16Tile<128>::kThreads, plan, args, s);
     }
   } else {
+    if (kind == DenseKind::kF32Split16) {
+      switch (d) {
+        case 64: return launch_all(attn_fwd_f32_split16<64, f32_split16_waves<64>()>, 64 * 8, plan, args, s);
+        case 96: return launch_all(attn_fwd_f32_split16<96, f32_split16_waves<96>()>, 64 * 8, plan, args, s);
+        case 128: return launch_all(attn_fwd_f32_split16<128, f32_split16_waves<128>()>, 64 * 8, plan, args, s);
+      }
+    }
     if (kind == DenseKind::kF32Split) {
       switch (d) {
         case 64: return launch_all(attn_fwd_f32_split<64, f32_split_waves<64>()>, f32_split_waves<64>() * 64, plan, args, s);
