@@ -340,6 +340,35 @@ def test_graph_capture_replays_match_eager(torch):
         run(torch, other.q, other.k, other.v, other.cu_seqlens, 16, 96, other.scale, 0, wl.BF16)
 
 
+def test_graph_capture_f32_key_split(torch):
+    """The f32 workload (one 256-token segment of 16 heads: 16-query key-split blocks)
+    captured into a HIP graph replays to the eager result bit for bit."""
+    from tests.gpu_helpers import from_device, to_device
+
+    case = wl.config_tiny()
+    assert mg.mgattn_dense_plan_block_m(case.cu_seqlens, case.n_seg, 16, 96, wl.F32, 0) == 16
+    want, _ = run(torch, case.q, case.k, case.v, case.cu_seqlens, 16, 96, case.scale, 0, wl.F32)
+    qd, kd, vd = (to_device(x, torch) for x in (case.q, case.k, case.v))
+    out = torch.zeros(case.T, 16 * 96, dtype=torch.float32, device="cuda")
+    cu = [int(x) for x in case.cu_seqlens]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mg.mgattn_dense(qd, kd, vd, out, cu, case.n_seg, 16, 96, case.scale, 0, wl.F32, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    say("graph capture, f32 key split")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mg.mgattn_dense(qd, kd, vd, out, cu, case.n_seg, 16, 96, case.scale, 0, wl.F32, torch.cuda.current_stream())
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(from_device(out, torch).reshape(want.shape), want), f"replay {rep} differs from eager"
+
+
 def test_graph_capture_key_split_shapes(torch):
     """Both key-split shapes captured into one HIP graph (a 1024-token segment of 16
     heads: 64-query tiles; a 2048-token one: 128-query tiles) replay to the eager
