@@ -108,6 +108,17 @@ __device__ inline float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Exchange with lane l^16 and combine (max or sum) -- one v_permlane16_swap: rows of 16
+// lanes 0 <-> 1 and 2 <-> 3.
+__device__ inline float row16_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float row16_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Key (relative to the 32-key block) held in accumulator register r by lane half hf.
 __device__ constexpr int acc_row(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 

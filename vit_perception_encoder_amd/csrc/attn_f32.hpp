@@ -383,17 +383,6 @@ void attn_fwd_f32_split(KernelArgs a) {
   }
 }
 
-// Exchange with lane l^16 and combine (max or sum) -- one v_permlane16_swap: rows of 16
-// lanes 0 <-> 1 and 2 <-> 3.
-__device__ inline float row16_swap_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float row16_swap_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // The same key split with one 16-query block per workgroup, for calls whose 32-query
 // blocks still leave CUs idle (a 256-token segment of 16 heads is 128 blocks of 32, 256
 // of 16): twice the workgroups, half the products per CU.  v_mfma_f32_16x16x4_f32, lane

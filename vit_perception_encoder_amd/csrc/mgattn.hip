@@ -304,9 +304,15 @@ int attend(const void* q, const void* k, const void* v, void* out, int64_t ldq, 
       args.nsplit = ns;
       args.part = ns > 1 ? static_cast<float*>(ws) : nullptr;
       void* params[] = {&args};
-      const void* kern = d == 64 ? reinterpret_cast<const void*>(attn_decode_bf16<64>)
-                         : d == 96 ? reinterpret_cast<const void*>(attn_decode_bf16<96>)
-                                   : reinterpret_cast<const void*>(attn_decode_bf16<128>);
+      // groups of up to 16 query heads: the 16-column tile (no zero columns)
+      const bool g16 = H / Hkv <= 16;
+      const void* kern =
+          g16 ? (d == 64 ? reinterpret_cast<const void*>(attn_decode_bf16_g16<64>)
+                : d == 96 ? reinterpret_cast<const void*>(attn_decode_bf16_g16<96>)
+                          : reinterpret_cast<const void*>(attn_decode_bf16_g16<128>))
+              : (d == 64 ? reinterpret_cast<const void*>(attn_decode_bf16<64>)
+                 : d == 96 ? reinterpret_cast<const void*>(attn_decode_bf16<96>)
+                           : reinterpret_cast<const void*>(attn_decode_bf16<128>));
       const unsigned wgs = static_cast<unsigned>(l.table.n * Hkv);
       if (hipLaunchKernel(kern, dim3(wgs * ns), dim3(DecodeTile<96>::kThreads), params, 0, s) != hipSuccess)
         return MGATTN_ERR_LAUNCH;
