@@ -181,9 +181,14 @@ static std::string pipe_case(int W, int kend) {
     };
     p.push_back({ISSUE, q, G::q_pad_dma_of(w, W, BM)});
     issue_tile(0);
-    if (ntiles > 1 && kPipePrologueTiles >= 2) issue_tile(1);
-    p.push_back({WAIT_LEAVE, -1, vd + (ntiles > 1 ? kd + vd : 0) + (mutated("pipe_prologue_short") ? 1 : 0)});
+    const bool early1 = kPipePrologueTiles >= 2;
+    if (ntiles > 1 && early1) issue_tile(1);
+    // wait for Q and K of tile 0 (V of tile 0 and, if issued, tile 1 stay in flight)
+    const bool old_count = mutated("pipe_prologue_old_count");  // a count still leaving tile 1 out
+    const int left = vd + (ntiles > 1 && (early1 || old_count) ? kd + vd : 0);
+    p.push_back({WAIT_LEAVE, -1, left + (mutated("pipe_prologue_short") ? 1 : 0)});
     p.push_back({BARRIER, -1, 0});
+    if (ntiles > 1 && !early1) issue_tile(1);  // tile 1 right after the first barrier
     p.push_back({READ, q, 0});
     p.push_back({READ, K[0], 0});  // QK of step 0
     if (nsteps > 1) p.push_back({READ, K[pipe_k_step(0) * SK / BN], 0});

@@ -41,6 +41,7 @@ def test_kernel_schedules_are_race_free(model):
     "pipe_sync_even",              # barriers on even iterations instead of odd
     "pipe_no_final_barrier",       # output staging over K/V another wave still reads
     "pipe_prologue_short",         # the prologue waits for one DMA too few
+    "pipe_prologue_old_count",     # tile 1 issued after the first barrier, the wait still leaving its DMA out
     "phased_issue_early",          # a stage refilled two phases early
     "phased_wait_late",            # a tile waited for two phases late
     "split_k_early",               # key-split: K of tile j+3 into the slot of K of tile j+1

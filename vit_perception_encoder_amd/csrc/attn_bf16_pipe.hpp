@@ -28,9 +28,9 @@
 // LDS: K of step s is read in iteration s-1, V of step s in iteration s+1, so tile t
 // (steps 2t, 2t+1) is live in iterations 2t-1 .. 2t+2.  One barrier per tile, at the
 // start of odd iteration 2t+1: each wave first waits for its own DMA of tile t+1
-// (issued two iterations earlier), and after the barrier tile t-1's stage (last read
-// in iteration 2t) receives tile t+2.  The Q tile arrives by DMA in the third stage
-// before tile 2 does.
+// (issued two iterations earlier; tile 1 just after the first barrier), and after the
+// barrier tile t-1's stage (last read in iteration 2t) receives tile t+2.  The Q tile
+// arrives by DMA in the third stage before tile 2 does.
 //
 // Rescaling is lazy (the running maximum moves only when a row's maximum grows by more
 // than 2^8 in probability terms, decided per wave) and branch-free inside the loop:
@@ -241,10 +241,13 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   const int my_kdma = KDMA / W + (wave < KDMA % W ? 1 : 0);
   const int my_vdma = VDMA / W + (wave < VDMA % W ? 1 : 0);
 
-  // ---- prologue: Q tile (from the third stage on), tiles 0 and 1.  Q rows and K of tile
-  // 0 are waited for before the first barrier; V of tile 0 and tile 1 at the barrier
-  // of iteration 1.  Key-split: Q after the K and V rings; K of tiles 0 and 1, then V
-  // of tile 0; K of tile 1 is waited for at the barrier of iteration 0.
+  // ---- prologue: Q tile (from the third stage on) and tile 0; Q rows and K of tile 0
+  // are waited for before the first barrier, V of tile 0 at the barrier of iteration 1.
+  // Tile 1 goes out right after the first barrier (also waited for at iteration 1):
+  // issued with the rest, its 50 KB per workgroup share the start-up burst of every
+  // workgroup at once and hold back the Q rows and K the first product waits for.
+  // Key-split: Q after the K and V rings; K of tiles 0 and 1, then V of tile 0; K of
+  // tile 1 is waited for at the barrier of iteration 0.
   // Q slot s (16 bytes) is row s/KSL, piece min(s%KSL, D/8-1), as for K
   constexpr int QDMA = TL::q_pad_dma(BM);
   constexpr int QDMA_W = (QDMA + W - 1) / W;
@@ -267,8 +270,7 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
   } else {
     issue_tile(0, 1);
     issue_tile(0, 2);
-    static_assert(sched::kPipePrologueTiles == 2, "tiles 0 and 1 before the first barrier");
-    if (ntiles > 1) issue_tile(1, 3);
+    static_assert(sched::kPipePrologueTiles == 1, "tile 0 before the first barrier, tile 1 right after it");
   }
   // RoPE angles of this lane's query, computed while the prologue's DMA is in flight:
   // fragment st holds channels 16st + 8hf + [0, 8), i.e. 4 pairs of one half of the
@@ -291,8 +293,11 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
       }
   }
   if constexpr (kSplit) dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma : 0));
-  else dma_wait_leave(my_vdma + (ntiles > 1 ? my_kdma + my_vdma : 0));
+  else dma_wait_leave(my_vdma);
   __syncthreads();
+  if constexpr (!kSplit) {
+    if (ntiles > 1) issue_tile(1, 3);
+  }
 
   bf16x8 qf[KS];
 #pragma unroll

@@ -68,14 +68,15 @@ constexpr MGATTN_HD int phased_wait_phase(int t, int steps_per_tile) { return 2 
 // ---- the pipelined kernel (attn_fwd_bf16_pipe): iteration j runs PV of step j-1, QK
 // of step j+1 and the softmax of step j; QK of step 0 runs before iteration 0.  Tile t
 // sits in stage t % 3; the Q tile (rows padded like K rows) starts at stage 2 and, for
-// 256 rows, runs past its end, until tile 2 arrives.  Tiles 0 and 1 are issued before
-// the first barrier, which publishes Q and K of tile 0; odd iterations open with a
-// wait for all of the wave's DMA, a barrier, and the issue of tile pipe_issue_tile(j).
+// 256 rows, runs past its end, until tile 2 arrives.  The Q tile and tile 0 are issued
+// before the first barrier, which publishes Q and K of tile 0, and tile 1 right after
+// it; odd iterations open with a wait for all of the wave's DMA, a barrier, and the
+// issue of tile pipe_issue_tile(j).
 constexpr MGATTN_HD int pipe_k_step(int j) { return j + 1; }       // K read by iteration j (QK)
 constexpr MGATTN_HD int pipe_v_step(int j) { return j - 1; }       // V read by iteration j (PV)
 constexpr MGATTN_HD bool pipe_syncs(int j) { return (j & 1) != 0; }
 constexpr MGATTN_HD int pipe_issue_tile(int j) { return (j >> 1) + 2; }
-constexpr int kPipePrologueTiles = 2;
+constexpr int kPipePrologueTiles = 1;  // tiles issued before the first barrier (tile 1 follows it)
 template <int D>
 constexpr MGATTN_HD int pipe_q_elem() { return (Geometry<D>::kStages - 1) * Geometry<D>::kStageElems; }
 template <int D>
