@@ -736,7 +736,12 @@ def main() -> int:
                 mg.mgattn_dense(q, k, v, out, cu, nseg, wl.HEADS, wl.HEAD_DIM, wl.SCALE, 0, mg.MGATTN_BF16, strm)
         return time_graph(torch, one_pass, n=1) / len(idx)
 
-    full_ms, win_ms = kind_ms(full_idx), kind_ms(win_idx)
+    # (--eager launches nothing through graphs: the eager events are the split there, and
+    # the i-th tower launch of the run stays layer i mod 50 for the counter summaries)
+    if graph is not None:
+        full_ms, win_ms = kind_ms(full_idx), kind_ms(win_idx)
+    else:
+        full_ms, win_ms = full_ms_e, win_ms_e
     full_tf = layers[full_idx[0]][5] / (full_ms * 1e-3) / 1e12
     win_tf = layers[win_idx[0]][5] / (win_ms * 1e-3) / 1e12
 
