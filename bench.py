@@ -200,6 +200,52 @@ def counter_table(paths) -> int:
     return 0
 
 
+def trace_table(path: str, steps: int, warmup: int) -> int:
+    """Markdown summary of the tower's attention launches in a rocprofv3 --kernel-trace
+    CSV of `bench.py --steps K --warmup W --no-token-path` (graph path): the launches in
+    start order fall into the parts main() runs them in -- W eager warm-up steps, one
+    side-stream step, W graph warm-up replays, the K timed replays, the eager breakdown
+    passes (max(3, min(K, 10)) steps), then the per-kind graphs -- 50 launches per step,
+    the i-th launch of a step being layer i of the schedule."""
+    from vit_perception_encoder_amd import workloads as wl
+    kinds = wl.tower_layer_kinds()
+    nl = len(kinds)
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            grid = int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0)
+            if _is_tower_kernel(r["Kernel_Name"], grid):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    nb = max(3, min(steps, 10))
+    parts = [("eager warm-up", warmup * nl), ("side-stream warm-up", nl), ("graph warm-up replays", warmup * nl),
+             ("**timed graph replays**", steps * nl), ("eager breakdown passes", nb * nl)]
+    durs = [(e - s) / 1e3 for s, e in rows]
+    print(f"{len(rows)} launches of {KERNEL_NAME}: mean {np.mean(durs):.2f} us, min {np.min(durs):.2f}, "
+          f"max {np.max(durs):.2f}\n")
+    print("| part | launches | mean kernel (us) | sum of kernels per step (us) | first start to last end per step (us) |")
+    print("|---|---|---|---|---|")
+    i = 0
+    timed = None
+    for name, n in parts:
+        seg = rows[i:i + n]
+        if len(seg) < n:
+            print(f"(trace ends inside part '{name}')")
+            return 1
+        per_step = [seg[s * nl:(s + 1) * nl] for s in range(n // nl)]
+        mean_k = np.mean([(e - s) / 1e3 for s, e in seg])
+        span = np.mean([(st[-1][1] - st[0][0]) / 1e3 for st in per_step])
+        print(f"| {name} | {n} | {mean_k:.2f} | {mean_k * nl:.1f} | {span:.1f} |")
+        if "timed" in name:
+            timed = seg
+        i += n
+    print(f"| per-kind graphs | {len(rows) - i} | {np.mean(durs[i:]):.2f} | | |")
+    full = [(e - s) / 1e3 for j, (s, e) in enumerate(timed) if kinds[j % nl] == "full"]
+    win = [(e - s) / 1e3 for j, (s, e) in enumerate(timed) if kinds[j % nl] == "window"]
+    print(f"\nIn the timed replays: full layers {np.mean(full):.2f} us, window layers {np.mean(win):.2f} us per launch.")
+    return 0
+
+
 def host_threads() -> int:
     """Every core this process may run on."""
     try:
@@ -614,6 +660,9 @@ def main() -> int:
                     help="print HBM traffic per dispatch of every kernel from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--counter-table", nargs="+", metavar="CSV",
                     help="print mean counters per tower launch (full / window) from rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--trace-table", nargs=3, metavar=("CSV", "STEPS", "WARMUP"),
+                    help="summarise the tower launches of a rocprofv3 --kernel-trace CSV of `bench.py --steps STEPS "
+                         "--warmup WARMUP --no-token-path` by part of the run and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration under rocprofv3)")
     ap.add_argument("--shape-sweep", action="store_true",
@@ -629,6 +678,8 @@ def main() -> int:
         return counter_table(args.counter_table)
     if args.kernel_traffic:
         return kernel_traffic(*args.kernel_traffic)
+    if args.trace_table:
+        return trace_table(args.trace_table[0], int(args.trace_table[1]), int(args.trace_table[2]))
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: mgattn has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2

@@ -114,3 +114,32 @@ def test_counter_summaries_on_synthetic_csv(tmp_path, monkeypatch):
     assert r.returncode == 0, r.stderr
     tower_row = next(x for x in r.stdout.splitlines() if f"| {bench.TOWER_GRID} |" in x and "attn_fwd" in x)
     assert "| 3 | 49.15 | 12.29 |" in tower_row, tower_row
+
+
+def test_trace_table_splits_the_run_into_its_parts(tmp_path, capsys):
+    """A synthetic kernel trace of `--steps 2 --warmup 1`: the timed replays (launches
+    250..349 of the tower kernel in start order) are the ones whose mean the table
+    reports as timed, full layers 100 us and window layers 30 us; other kernels and other
+    grids are ignored."""
+    from vit_perception_encoder_amd import workloads as wl
+    kinds = wl.tower_layer_kinds()
+    path = tmp_path / "kernel_trace.csv"
+    t = 0
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Grid_Size", "Start_Timestamp", "End_Timestamp"])
+        # parts: 1 eager warm-up step, 1 side step, 1 graph warm-up, 2 timed, 3 breakdown, 1 per-kind
+        for part, nsteps in enumerate((1, 1, 1, 2, 3, 1)):
+            for _ in range(nsteps):
+                for layer in range(50):
+                    dur = (100 if kinds[layer] == "full" else 30) * (1 if part == 3 else 2)
+                    w.writerow([f"void mgattn::{bench.KERNEL_NAME}(mgattn::KernelArgs)", bench.TOWER_GRID, t,
+                                t + dur * 1000])
+                    w.writerow(["other_kernel", 64, t, t + 5000])
+                    t += dur * 1000 + 2000
+    assert bench.trace_table(str(path), 2, 1) == 0
+    out = capsys.readouterr().out
+    timed = [line for line in out.splitlines() if "timed graph replays" in line][0].split("|")
+    mean_timed = (13 * 100 + 37 * 30) / 50
+    assert int(timed[2]) == 100 and abs(float(timed[3]) - mean_timed) < 0.01
+    assert "full layers 100.00 us, window layers 30.00 us" in out

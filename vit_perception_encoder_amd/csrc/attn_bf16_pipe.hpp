@@ -60,6 +60,17 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(std::make_integer_sequence<int, N>{}, static_cast<F&&>(f));
 }
 
+// Row maxima in the main loop: IEEE maximum (NaN in, NaN out), which gfx950 has as
+// v_maximum3_f32.  fmaxf (NaN ignored) makes the compiler quiet every MFMA result
+// with a v_max_f32 x, x before it enters a maximum chain: 8 VALU instructions per
+// 64-key step that this form does not need.  Finite scores and -inf (masked keys) give
+// the same maxima either way; a NaN score makes the row NaN either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float half_swap_maximum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Scheduling fence: the compiler moves no instruction across it.
 #define MGATTN_FENCE() __builtin_amdgcn_sched_barrier(0)
 
@@ -435,24 +446,24 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
         if constexpr (k < 4) {
           static_for<2 * NB>([&](auto cc) {
             constexpr int ch = decltype(cc)::value, b = ch / 2, r0 = 8 * (ch % 2);
-            if constexpr (k == 0) mx[ch] = fmaxf(fmaxf(sc[b][r0], sc[b][r0 + 1]), sc[b][r0 + 2]);
-            if constexpr (k == 1) mx[ch] = fmaxf(fmaxf(mx[ch], sc[b][r0 + 3]), sc[b][r0 + 4]);
-            if constexpr (k == 2) mx[ch] = fmaxf(fmaxf(mx[ch], sc[b][r0 + 5]), sc[b][r0 + 6]);
-            if constexpr (k == 3) mx[ch] = fmaxf(mx[ch], sc[b][r0 + 7]);
+            if constexpr (k == 0) mx[ch] = vmax(vmax(sc[b][r0], sc[b][r0 + 1]), sc[b][r0 + 2]);
+            if constexpr (k == 1) mx[ch] = vmax(vmax(mx[ch], sc[b][r0 + 3]), sc[b][r0 + 4]);
+            if constexpr (k == 2) mx[ch] = vmax(vmax(mx[ch], sc[b][r0 + 5]), sc[b][r0 + 6]);
+            if constexpr (k == 3) mx[ch] = vmax(mx[ch], sc[b][r0 + 7]);
           });
         }
         if constexpr (k == 4) {
           // a step with no visible key for some rows (causal, or a key group past the
           // segment end) has maximum -inf; the floor keeps the reference finite (those
           // rows get p = 0 and take alpha = 0 at the first step with keys)
-          float mxa = fmaxf(mx[0], mx[1]);
-          if constexpr (NB == 2) mxa = fmaxf(mxa, fmaxf(mx[2], mx[3]));
-          const float m_blk = fmaxf(half_swap_max(mxa), -1.0e30f);
+          float mxa = vmax(mx[0], mx[1]);
+          if constexpr (NB == 2) mxa = vmax(mxa, vmax(mx[2], mx[3]));
+          const float m_blk = vmax(half_swap_maximum(mxa), -1.0e30f);
           if constexpr (FIRST) {
             m_run = m_blk;
           } else {
             const bool grow = __builtin_amdgcn_ballot_w64((m_blk - m_run) * c > kRescaleLog2) != 0;
-            const float m_new = grow ? fmaxf(m_run, m_blk) : m_run;
+            const float m_new = grow ? vmax(m_run, m_blk) : m_run;
             alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
             resc = grow;
             m_run = m_new;
