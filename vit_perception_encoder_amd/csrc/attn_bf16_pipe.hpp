@@ -98,7 +98,8 @@ struct PipeTile {
   // block 1 from slot kNPV + kKS on.
   static constexpr int qk_b(int i) { return i / kKS; }
   static constexpr int qk_s(int i) { return i % kKS; }
-  // Softmax slices: slots 0..3 the row maxima, slot 4 the running maximum; score pair
+  // Softmax slices: slots 0..3 the row maxima (64-key steps: block 0 in slots 0-1, block
+  // 1 in slots 2-3), slot 4 the running maximum; score pair
   // u (of the lane's 16 NB: block u/8) is exponentiated in slot exp_slot(u) and
   // converted to bf16 and summed one slot later; the row sum takes the step in slot
   // kLSlot.  NB = 2: S and P have one buffer each; block 0's pairs end before slot kNPV
@@ -441,15 +442,24 @@ void attn_fwd_bf16_pipe(KernelArgs a) {
       if constexpr (QK && k + DK >= NPV && k + DK < NSLOT) kf[k + DK - NPV] = read_k(ks, k + DK - NPV);
       // -- the softmax slice of slot k
       if constexpr (SM) {
-        // slots 0..3: row maximum as 2 NB independent max3 chains over 8 scores each
+        // slots 0..3: row maximum as 2 NB independent maximum chains over 8 scores each
         const f32x16(&sc)[NB] = s[BC];
         if constexpr (k < 4) {
           static_for<2 * NB>([&](auto cc) {
             constexpr int ch = decltype(cc)::value, b = ch / 2, r0 = 8 * (ch % 2);
-            if constexpr (k == 0) mx[ch] = vmax(vmax(sc[b][r0], sc[b][r0 + 1]), sc[b][r0 + 2]);
-            if constexpr (k == 1) mx[ch] = vmax(vmax(mx[ch], sc[b][r0 + 3]), sc[b][r0 + 4]);
-            if constexpr (k == 2) mx[ch] = vmax(vmax(mx[ch], sc[b][r0 + 5]), sc[b][r0 + 6]);
-            if constexpr (k == 3) mx[ch] = vmax(mx[ch], sc[b][r0 + 7]);
+            if constexpr (NB == 2) {
+              // block b in slots 2b and 2b+1: block 1, completed by the last QK MFMA of the
+              // previous iteration, is first read two slots after block 0
+              if constexpr (k == 2 * b)
+                mx[ch] = vmax(vmax(vmax(vmax(sc[b][r0], sc[b][r0 + 1]), sc[b][r0 + 2]), sc[b][r0 + 3]), sc[b][r0 + 4]);
+              if constexpr (k == 2 * b + 1)
+                mx[ch] = vmax(vmax(vmax(mx[ch], sc[b][r0 + 5]), sc[b][r0 + 6]), sc[b][r0 + 7]);
+            } else {
+              if constexpr (k == 0) mx[ch] = vmax(vmax(sc[b][r0], sc[b][r0 + 1]), sc[b][r0 + 2]);
+              if constexpr (k == 1) mx[ch] = vmax(vmax(mx[ch], sc[b][r0 + 3]), sc[b][r0 + 4]);
+              if constexpr (k == 2) mx[ch] = vmax(vmax(mx[ch], sc[b][r0 + 5]), sc[b][r0 + 6]);
+              if constexpr (k == 3) mx[ch] = vmax(mx[ch], sc[b][r0 + 7]);
+            }
           });
         }
         if constexpr (k == 4) {
