@@ -146,54 +146,52 @@ struct RopeArgs {
 };
 
 // One wave = one token, in place.  The token's patch position is wave-uniform and
-// computed once; lane j < d/2 computes cos and sin of rotation pair j (pairs below d/4
-// rotate by the column, the rest by the row, frequency index j mod d/4), and every
-// 16-byte piece of the token's H*d values (8 bf16 or 4 f32: whole pairs of one half
-// of a head, as d/2 is a multiple of 8) takes its pairs' values from those lanes by
-// lane shuffles, made with every lane active before the bounds test.
+// computed once.  A head's H*d values are P = d*elem/16 pieces of 16 bytes (8 bf16 or 4
+// f32: whole pairs of one half of a head, as d/2 is a multiple of 8), and lane l < G*P,
+// G = 64/P, always takes piece l mod P of head l/P of each group of G heads, so the
+// cosines and sines of its pieces' pairs (pairs below d/4 rotate by the column, the rest
+// by the row, frequency index pair mod d/4) are computed once per token in the lane
+// that uses them, and a group's G*P pieces are one contiguous stretch of the row.
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
   constexpr int kPer = 16 / sizeof(T);  // values per piece
-  constexpr int kPairs = kPer / 2;
+  constexpr int kPairs = kPer / 2;      // rotation pairs per piece
   const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * 4 + (threadIdx.x >> 6));
   if (t >= n_tokens) return;
   const int lane = threadIdx.x & 63;
+  const int P = a.pieces, G = 64 / P;  // pieces per head, heads per group (P <= 32)
+  const int g = lane / P, pc = lane - g * P;
+  const bool active = g < G;
   int prow = 0, pcol = 0;
   token_patch(a.tb, a.win, t, &prow, &pcol);
   const int quarter = a.d / 4;  // pairs per half of a head
-  const float f_l = a.inv_freq[lane < 2 * quarter ? lane % quarter : 0];  // loaded before the data
-  float c_l = 1.0f, s_l = 0.0f;
   T* row = static_cast<T*>(a.x) + static_cast<int64_t>(t) * a.ld;
-  const int total = a.H * a.pieces;
-  constexpr int kU = 4;  // pieces per lane loaded together
-  for (int j0 = 0; j0 < total; j0 += 64 * kU) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kU = 4;  // head groups per trip, their loads in flight together
+  float cs[kPairs], sn[kPairs];
+  for (int h0 = 0; h0 < a.H; h0 += G * kU) {
     u32x4 raw[kU];
-    int off[kU], pcs[kU];
+    int off[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int j = min(j0 + u * 64 + lane, total - 1);  // past the end: re-read the last piece
-      const int head = j / a.pieces;
-      pcs[u] = j - head * a.pieces;
-      off[u] = head * a.d + pcs[u] * kPer;
+      const int head = min(h0 + u * G + g, a.H - 1);  // inactive lanes and heads past the end re-read a piece
+      off[u] = head * a.d + pc * kPer;
       raw[u] = *reinterpret_cast<const u32x4*>(row + off[u]);
     }
-    if (j0 == 0 && lane < 2 * quarter) {  // the angles, while the first loads are in flight
-      const float pos = static_cast<float>(lane < quarter ? pcol + 1 : prow + 1);
-      if constexpr (sizeof(T) == 2) rope_angle_bf16(pos, f_l, &c_l, &s_l);
-      else rope_angle(pos, f_l, &c_l, &s_l);
+    if (h0 == 0) {  // the angles of this lane's pairs, while the first loads are in flight
+#pragma unroll
+      for (int k = 0; k < kPairs; ++k) {
+        const int pair = pc * kPairs + k;
+        const float pos = static_cast<float>(pair < quarter ? pcol + 1 : prow + 1);
+        const float f = a.inv_freq[pair % quarter];
+        if constexpr (sizeof(T) == 2) rope_angle_bf16(pos, f, &cs[k], &sn[k]);
+        else rope_angle(pos, f, &cs[k], &sn[k]);
+      }
     }
     asm volatile("" ::"v"(raw[0]), "v"(raw[1]), "v"(raw[2]), "v"(raw[3]));
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      float cs[kPairs], sn[kPairs];
-#pragma unroll
-      for (int k = 0; k < kPairs; ++k) {  // every lane active here
-        const int src = (pcs[u] * kPairs + k) & 63;
-        cs[k] = __shfl(c_l, src);
-        sn[k] = __shfl(s_l, src);
-      }
       uint32_t w[4] = {raw[u][0], raw[u][1], raw[u][2], raw[u][3]};
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -207,7 +205,7 @@ void rope2d_kernel(RopeArgs a, int32_t n_tokens) {
           w[2 * k + 1] = __float_as_uint(__builtin_fmaf(re, sn[k], imc));
         }
       }
-      if (j0 + u * 64 + lane < total) *reinterpret_cast<u32x4*>(row + off[u]) = u32x4{w[0], w[1], w[2], w[3]};
+      if (active && h0 + u * G + g < a.H) *reinterpret_cast<u32x4*>(row + off[u]) = u32x4{w[0], w[1], w[2], w[3]};
     }
   }
 }
