@@ -137,6 +137,33 @@ def test_rope2d_other_head_dims(torch, d):
     _check_rope(from_device(xd, torch), W.rope2d(wl.bf16_bits_to_f32(x), grids, 4, H, d, THETA), H, d, wl.BF16)
 
 
+@pytest.mark.parametrize("dtype,d,H", [(wl.BF16, 16, 37), (wl.BF16, 32, 5), (wl.BF16, 48, 11), (wl.F32, 16, 9),
+                                       (wl.F32, 64, 3), (wl.F32, 128, 5)])
+def test_rope2d_piece_groups(torch, dtype, d, H):
+    """The pass gives each lane one 16-byte piece position of a head (P = d*elem/16
+    pieces per head, 64/P heads per group of lanes).  Every head dim's layout, from 2
+    pieces and 32 heads per group to 32 pieces and 2 heads, with head counts that leave
+    the last group partial, on rows padded past H*d: the heads match the oracle and the
+    padding is left untouched."""
+    grids, win = [(9, 11)], 4
+    T = _tokens(grids)
+    elem = 2 if dtype == wl.BF16 else 4
+    ld = H * d + 3 * (16 // elem)  # three 16-byte pieces of padding per row
+    say(f"rope2d piece groups dtype={dtype} d={d} H={H}")
+    x = wl.normal_f32(760 + d + H, (T, ld))
+    if dtype == wl.BF16:
+        x = wl.f32_to_bf16_bits(x)
+        xin = wl.bf16_bits_to_f32(x).astype(np.float64)
+    else:
+        xin = x.astype(np.float64)
+    xd = to_device(x, torch)
+    mg.mgattn_rope2d(xd, ld, grids, win, H, d, THETA, dtype, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    got = from_device(xd, torch)
+    _check_rope(got[:, :H * d], W.rope2d(xin[:, :H * d], grids, win, H, d, THETA), H, d, dtype)
+    assert np.array_equal(got[:, H * d:], xin[:, H * d:]), "the pass wrote into the row padding"
+
+
 def test_rope2d_in_place_on_merged_qkv(torch):
     H, d, grids, win = 16, 96, [(40, 40), (9, 33)], 32
     T, row = _tokens(grids), H * d
